@@ -1,0 +1,223 @@
+"""Plain float64 CPU oracle for paged KV-cache decode attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the product path.  No torch, no code
+shared with the HIP library.
+
+Array conventions (all numpy):
+
+* caches ``k_cache`` / ``v_cache``: ``[num_blocks, kv_heads, block_size, head_dim]``
+  for one layer; element type float32, or uint16 holding bfloat16 bit patterns;
+* ``block_tables``: int ``[num_seqs, max_blocks_per_seq]``, physical block ids in
+  logical order;
+* ``seq_lens``: int ``[num_seqs]``, number of cached positions each query sees;
+* ``q``: ``[num_seqs, num_heads, head_dim]`` (same element type as the caches).
+
+Decode results are float64.  Append and block copy work on the raw element
+bits, so they are exact for either element type.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Capacity arithmetic and address translation
+# --------------------------------------------------------------------------
+
+def block_layout(tokens: int, block_size: int) -> tuple[int, int]:
+    """Blocks one unshared sequence occupies, and its unused tail slots.
+
+    lihaoran.work PagedAttention explainer, section "How many tail slots
+    remain unused?": a sequence of T cached positions in blocks of b slots
+    needs the ceiling of T/b blocks; the slots left over are that many
+    blocks' capacity minus T, which lies in [0, b-1] for T > 0, and an empty
+    sequence takes no block at all.  A negative token count or a block size
+    that is not positive is an error (ValueError).
+    """
+    if tokens < 0 or block_size <= 0:
+        raise ValueError(f"block_layout: bad sizes tokens={tokens} block_size={block_size}")
+    whole, leftover = divmod(tokens, block_size)
+    blocks = whole if leftover == 0 else whole + 1
+    return blocks, blocks * block_size - tokens
+
+
+def translate(table_row, position: int, block_size: int) -> tuple[int, int]:
+    """Physical (block, slot) that holds cached position ``position``.
+
+    lihaoran.work PagedAttention explainer, section "A block table maps
+    logical order to physical storage": the logical block of zero-based
+    position t is t // b, the slot inside it is t % b, and the table entry
+    for that logical block names the physical block.
+    """
+    logical = position // block_size
+    slot = position - logical * block_size
+    return int(table_row[logical]), int(slot)
+
+
+# --------------------------------------------------------------------------
+# Element decoding
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns (uint16) as float64.
+
+    A bfloat16 is the upper 16 bits of an IEEE-754 binary32, so widening the
+    pattern to 32 bits with 16 zero bits below gives the same number.
+    """
+    wide = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return wide.view(np.float32).astype(np.float64)
+
+
+def to_f64(x: np.ndarray) -> np.ndarray:
+    """float32 arrays as float64; uint16 arrays read as bfloat16 bits."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    if x.dtype in (np.float32, np.float64):
+        return x.astype(np.float64)
+    raise TypeError(f"oracle: unsupported element type {x.dtype}")
+
+
+# --------------------------------------------------------------------------
+# Gather through the block table
+# --------------------------------------------------------------------------
+
+def gather_history(k_cache, v_cache, table_row, seq_len: int, block_size: int):
+    """Logical K and V history of one sequence, one position at a time.
+
+    Follows the conceptual lookup on the zenaique.com page (code box
+    "Conceptual: PagedAttention block lookup"): every position of
+    [0, seq_len) is sent through the block table to its physical block and
+    slot, and that slot's keys and values (all KV heads) are taken in
+    position order.  Returns float64 arrays ``[seq_len, kv_heads, head_dim]``.
+    """
+    _, kv_heads, _, head_dim = k_cache.shape
+    keys = np.empty((seq_len, kv_heads, head_dim), dtype=np.float64)
+    values = np.empty((seq_len, kv_heads, head_dim), dtype=np.float64)
+    for position in range(seq_len):
+        block, slot = translate(table_row, position, block_size)
+        keys[position] = to_f64(k_cache[block, :, slot, :])
+        values[position] = to_f64(v_cache[block, :, slot, :])
+    return keys, values
+
+
+def gather_history_vectorised(k_cache, v_cache, table_row, seq_len: int, block_size: int):
+    """Same result as :func:`gather_history`, with numpy fancy indexing.
+
+    Used for the large synthetic batches; a test checks it against the
+    position-by-position loop.
+    """
+    positions = np.arange(seq_len, dtype=np.int64)
+    blocks = np.asarray(table_row, dtype=np.int64)[positions // block_size]
+    slots = positions % block_size
+    keys = to_f64(k_cache[blocks, :, slots, :])
+    values = to_f64(v_cache[blocks, :, slots, :])
+    return keys, values
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+
+def attend(q_heads, keys, values, scale: float) -> np.ndarray:
+    """Scaled dot-product attention of one decode query over its history.
+
+    ``q_heads`` ``[num_heads, head_dim]``; ``keys``/``values``
+    ``[seq_len, kv_heads, head_dim]``, all float64.
+
+    The zenaique.com lookup code ends in ordinary scaled dot-product
+    attention over the gathered keys and values, and the lihaoran.work
+    explainer (section "A block table maps logical order to physical
+    storage") states that attention still spans the whole visible history,
+    so every one of the seq_len positions takes part.  Grouped-query
+    attention: with G = num_heads / kv_heads, query head h reads KV head
+    h // G (consecutive query heads share a KV head).  The softmax subtracts
+    the row maximum before exponentiating, which leaves the result unchanged
+    and keeps exp() finite.  An empty history gives a zero output.
+    """
+    num_heads, head_dim = q_heads.shape
+    seq_len, kv_heads, _ = keys.shape
+    if num_heads % kv_heads != 0:
+        raise ValueError("num_heads must be a multiple of kv_heads")
+    group = num_heads // kv_heads
+    out = np.zeros((num_heads, head_dim), dtype=np.float64)
+    if seq_len == 0:
+        return out
+    for head in range(num_heads):
+        kv_head = head // group
+        scores = scale * (keys[:, kv_head, :] @ q_heads[head])
+        weights = np.exp(scores - scores.max())
+        weights = weights / weights.sum()
+        out[head] = weights @ values[:, kv_head, :]
+    return out
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, block_size: int,
+                 seqs=None, literal: bool = False) -> np.ndarray:
+    """Decode attention for every sequence (or the listed ``seqs``).
+
+    For each sequence: gather its history through its block table, then
+    :func:`attend`.  ``literal=True`` uses the position-by-position gather.
+    Returns float64 ``[len(seqs), num_heads, head_dim]``.
+    """
+    q = np.asarray(q)
+    if seqs is None:
+        seqs = range(q.shape[0])
+    seqs = list(seqs)
+    gather = gather_history if literal else gather_history_vectorised
+    out = np.empty((len(seqs), q.shape[1], q.shape[2]), dtype=np.float64)
+    for i, s in enumerate(seqs):
+        keys, values = gather(k_cache, v_cache, block_tables[s], int(seq_lens[s]), block_size)
+        out[i] = attend(to_f64(q[s]), keys, values, scale)
+    return out
+
+
+def contiguous_decode(q, keys_per_seq, values_per_seq, scale: float) -> np.ndarray:
+    """Decode attention over histories stored contiguously (no paging).
+
+    The unpaged baseline the paged kernel must reproduce: the lihaoran.work
+    explainer notes paging changes where the data lives, not what attention
+    computes.  ``keys_per_seq[s]`` is ``[seq_len_s, kv_heads, head_dim]``.
+    """
+    q = np.asarray(q)
+    out = np.empty(q.shape, dtype=np.float64)
+    for s in range(q.shape[0]):
+        out[s] = attend(to_f64(q[s]), to_f64(keys_per_seq[s]), to_f64(values_per_seq[s]), scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Cache writes
+# --------------------------------------------------------------------------
+
+def kv_append(k_cache, v_cache, k_new, v_new, slot_mapping, block_size: int) -> None:
+    """Write new tokens' keys and values into their cache slots, in place.
+
+    "How PagedAttention works", section "A strong answer": each decode step
+    adds one token to a sequence's cache.  A slot number s names physical
+    block s // b, position s % b inside it (the same block/offset split as
+    the block table translation); a negative slot is padding and is skipped.
+    Works on raw element bits, so the copy is exact.
+    """
+    for token, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        block, offset = divmod(int(slot), block_size)
+        k_cache[block, :, offset, :] = k_new[token]
+        v_cache[block, :, offset, :] = v_new[token]
+
+
+def copy_blocks(k_cache, v_cache, pairs) -> None:
+    """Copy-on-write block copy, in place.
+
+    "How PagedAttention works", feature table row on beam search / parallel
+    sampling, and the zenaique.com follow-up on beam search: when a shared
+    block is about to diverge, a fresh block receives a full copy of it.
+    Each (src, dst) pair copies every KV head and every slot of block src,
+    keys and values, into block dst.  Destinations never overlap sources.
+    """
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        k_cache[dst] = k_cache[src]
+        v_cache[dst] = v_cache[src]

@@ -1,0 +1,208 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged KV-cache decode attention for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (PagedAttention): a sequence's cached keys and values live in
+ * fixed-size physical blocks of `block_size` token slots, not in one
+ * contiguous slab; a per-sequence block table lists, in logical order, the
+ * physical block that holds each run of `block_size` positions.  Zero-based
+ * position t lives in logical block t / block_size at slot t % block_size.
+ * ("How PagedAttention works", aiinfrainterviews.com, sections "TL;DR" and
+ * "A strong answer"; lihaoran.work PagedAttention explainer, section "A block
+ * table maps logical order to physical storage".)
+ *
+ * Common conventions for every entry point below
+ * ----------------------------------------------
+ * Memory.  Every array argument is DEVICE memory owned by the caller, in the
+ * layout stated (C order, densely packed), aligned to 16 bytes.  The library
+ * allocates nothing, frees nothing and keeps no state between calls.
+ *
+ * One layer's cache.  `k_cache` and `v_cache` are each
+ *     [num_blocks][kv_heads][block_size][head_dim]
+ * elements of the call's dtype: physical block p holds, for each KV head,
+ * block_size consecutive token slots of head_dim elements.
+ *
+ * dtype.  PA_F32 (IEEE binary32) or PA_BF16 (bfloat16).  q, out, caches and
+ * new tokens of one call share the dtype.  Arithmetic is in fp32 either way.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ * asynchronous and ordered on that stream; nothing synchronises the host.
+ *
+ * Errors.  Host-side arguments are checked before anything is launched:
+ *   PA_ERR_INVALID_ARG  a size is negative or zero where it must be positive,
+ *                       a pointer is NULL or not 16-byte aligned, head counts
+ *                       do not divide, a workspace is too small (the same
+ *                       convention as the explainer's block_layout, which
+ *                       rejects negative sizes);
+ *   PA_ERR_UNSUPPORTED  a shape with no kernel instance (see each call);
+ *   PA_ERR_HIP          the HIP runtime reported a launch error.
+ * On an error nothing has been launched (PA_ERR_HIP: possibly part of it).
+ * Device-resident contents (table entries, slots, lengths) are read by the
+ * kernels, which never access memory outside the arrays described here:
+ * see each call for what happens to out-of-range contents.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,
+  PA_ERR_UNSUPPORTED = 2,
+  PA_ERR_HIP = 3
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Decode kernel selection for pa_decode_ex. */
+typedef enum pa_kernel {
+  PA_KERNEL_AUTO = 0,  /* MFMA kernel when it supports the shape, else VALU  */
+  PA_KERNEL_VALU = 1,  /* vector-ALU kernel: any supported shape and dtype   */
+  PA_KERNEL_MFMA = 2   /* matrix-core kernel: bf16, head_dim 64/128,
+                          block_size 16..256, num_heads/kv_heads <= 16       */
+} pa_kernel;
+
+/* Version of this ABI (increments on any signature change). */
+int32_t pa_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* pa_status_string(int32_t status);
+
+/*
+ * Host helper: blocks an unshared sequence of `tokens` cached positions
+ * occupies, and the unused slots in its last block
+ * (lihaoran.work explainer, section "How many tail slots remain unused?":
+ * blocks = ceil(tokens / block_size), unused = blocks*block_size - tokens,
+ * which is in [0, block_size-1] for tokens > 0 and 0 for tokens = 0).
+ * `blocks` and `unused` are HOST pointers.  tokens < 0 or block_size <= 0
+ * gives PA_ERR_INVALID_ARG and leaves the outputs untouched.
+ */
+pa_status pa_block_layout(int64_t tokens, int32_t block_size, int64_t* blocks, int64_t* unused);
+
+/*
+ * KV append: write the keys and values of `num_tokens` new tokens into the
+ * cache slots named by `slot_mapping` ("How PagedAttention works", section
+ * "A strong answer": a sequence's cache grows by one token per decode step).
+ *
+ *   k_new, v_new   [num_tokens][kv_heads][head_dim], dtype
+ *   k_cache,       [num_blocks][kv_heads][block_size][head_dim], written in place
+ *   v_cache
+ *   slot_mapping   int64 [num_tokens]: slot s means physical block
+ *                  s / block_size, slot s % block_size.  s < 0 marks a padding
+ *                  token and is skipped; s >= num_blocks*block_size is also
+ *                  skipped (never written out of bounds).
+ *
+ * The copy is bit-exact.  Slots must be distinct (two tokens writing one slot
+ * race).  num_tokens = 0 launches nothing.  Shapes: head_dim*elem_size a
+ * multiple of 16 bytes (head_dim in {64, 128} is instantiated for both
+ * dtypes; any multiple of 8 for bf16 / 4 for fp32 works), block_size >= 1.
+ */
+pa_status pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                       int32_t kv_heads, int32_t block_size, int32_t head_dim, int32_t dtype,
+                       void* stream);
+
+/*
+ * Decode plan: the partition size, the number of partitions and the workspace
+ * size that pa_decode/pa_decode_ex will use for these host-side sizes.  All
+ * outputs are HOST pointers (any may be NULL).
+ *
+ * Split-sequence decode: each sequence's history is cut into partitions of
+ * `partition_size` tokens, one workgroup per (sequence, KV head, partition);
+ * when a sequence spans more than one partition, each writes a partial result
+ * (running max, running sum, unnormalised output) to the workspace and a
+ * second kernel merges them.
+ *   partition_size > 0 : used as given by the VALU kernel; rounded up to a
+ *                        multiple of 32 tokens by the MFMA kernel;
+ *   partition_size = 0 : chosen by the library from num_seqs*kv_heads and
+ *                        max_seq_len (no split when there are enough
+ *                        (sequence, head) pairs to fill the GPU).
+ * workspace bytes = num_seqs*num_heads*num_partitions*(head_dim+2)*4 when
+ * num_partitions > 1, else 0.
+ */
+pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t max_seq_len, int32_t partition_size,
+                         int32_t dtype, int32_t kernel, int32_t* eff_partition_size,
+                         int32_t* num_partitions, size_t* workspace_bytes);
+
+/* Workspace bytes pa_decode needs (0 on invalid arguments). */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                                 int32_t partition_size, int32_t dtype);
+
+/*
+ * Paged decode attention for one layer: one query token per sequence attends
+ * over all of that sequence's cached positions [0, seq_lens[s]), gathered
+ * through its block table (zenaique.com page, conceptual block-lookup code;
+ * lihaoran.work explainer, section "A block table maps logical order to
+ * physical storage").
+ *
+ *   out           [num_seqs][num_heads][head_dim], dtype, written
+ *   q             [num_seqs][num_heads][head_dim], dtype
+ *   k_cache,      [num_blocks][kv_heads][block_size][head_dim], dtype, read only
+ *   v_cache
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries past a
+ *                 sequence's last block are never read
+ *   seq_lens      int32 [num_seqs]
+ *   max_seq_len   host upper bound of seq_lens (sizes the grid)
+ *   scale         multiplies q.k before the softmax (e.g. 1/sqrt(head_dim))
+ *   workspace     device scratch of at least pa_decode_workspace_bytes();
+ *                 may be NULL when that is 0.  Contents need no initialising.
+ *
+ * out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t][h / G]) * V[t][h / G]
+ * with G = num_heads / kv_heads (query head h reads KV head h / G), K[t]/V[t]
+ * the key/value rows of position t.  seq_lens[s] = 0 gives a zero row.
+ * Out-of-range device contents produce NaN rows instead of out-of-bounds
+ * reads: a sequence with seq_lens[s] < 0, > max_seq_len or
+ * > max_blocks_per_seq*block_size, or whose table names a block outside
+ * [0, num_blocks), gets NaN in all of its heads' outputs.
+ * `out` must not alias any input.  Shapes: head_dim in {64, 128};
+ * block_size a power of two in [1, 256]; num_heads % kv_heads == 0 with
+ * G in {1, 2, 4, 8, 16}.
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                    int32_t num_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, float scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, int32_t dtype, void* stream);
+
+/* pa_decode with an explicit kernel choice (pa_kernel).  PA_KERNEL_MFMA on a
+ * shape it does not support returns PA_ERR_UNSUPPORTED. */
+pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                       int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, float scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       int32_t dtype, int32_t kernel, void* stream);
+
+/*
+ * Copy-on-write block copy: for each (src, dst) pair, copy every KV head and
+ * every slot of physical block src into physical block dst, in both caches
+ * ("How PagedAttention works", feature table row on beam search and parallel
+ * sampling; zenaique.com follow-up on beam search: a fork shares blocks and
+ * copies only the block that diverges, into a freshly allocated block).
+ *
+ *   k_cache, v_cache  [num_blocks][kv_heads][block_size][head_dim], in place
+ *   block_mapping     int64 [num_pairs][2] = (src, dst)
+ *
+ * Bit-exact.  The dst ids must be distinct and disjoint from the src ids
+ * (otherwise the result depends on ordering).  A pair with either id outside
+ * [0, num_blocks) is skipped.  num_pairs = 0 launches nothing.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t num_blocks, int32_t kv_heads,
+                         int32_t block_size, int32_t head_dim, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

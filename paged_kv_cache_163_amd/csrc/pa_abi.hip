@@ -1,0 +1,259 @@
+// C ABI of libpa.so (declared in include/pa.h): argument checks, decode
+// planning (partition size, grid, workspace) and kernel dispatch.  Every check
+// on host-side arguments runs before the first HIP call, so a rejected call
+// never touches the device.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+// Work-groups a decode launch should offer before sequences are split: four
+// four-wave work-groups per compute unit on a 256-CU MI355X.
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int32_t kMfmaStep = 32;  // tokens per MFMA-kernel step
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int32_t log2i(int64_t v) {
+  int32_t s = 0;
+  while ((int64_t(1) << s) < v) ++s;
+  return s;
+}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+int32_t elem_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+
+struct Plan {
+  int32_t kernel;      // PA_KERNEL_VALU or PA_KERNEL_MFMA
+  int32_t partition;   // tokens per partition
+  int32_t partitions;  // grid extent along partitions
+  size_t workspace;    // bytes
+};
+
+bool valu_supports(int32_t dtype, int32_t head_dim, int32_t group, int32_t block_size) {
+  (void)dtype;
+  return (head_dim == 64 || head_dim == 128) &&
+         (group == 1 || group == 2 || group == 4 || group == 8) && pow2(block_size) &&
+         block_size <= 256;
+}
+
+bool mfma_supports(int32_t dtype, int32_t head_dim, int32_t group, int32_t block_size) {
+  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && group >= 1 && group <= 16 &&
+         pow2(block_size) && block_size >= 16 && block_size <= 256;
+}
+
+pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_seq_len, int32_t partition_size,
+                    int32_t dtype, int32_t kernel, Plan* plan) {
+  if (num_seqs < 0 || num_heads <= 0 || kv_heads <= 0 || num_heads % kv_heads != 0 ||
+      head_dim <= 0 || block_size <= 0 || max_seq_len < 0 || partition_size < 0 ||
+      !dtype_ok(dtype))
+    return PA_ERR_INVALID_ARG;
+  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
+    return PA_ERR_INVALID_ARG;
+  if (!pow2(block_size) || block_size > 256) return PA_ERR_UNSUPPORTED;
+  const int32_t group = num_heads / kv_heads;
+  const bool mfma = mfma_supports(dtype, head_dim, group, block_size);
+  const bool valu = valu_supports(dtype, head_dim, group, block_size);
+  int32_t chosen;
+  if (kernel == PA_KERNEL_MFMA) {
+    if (!mfma) return PA_ERR_UNSUPPORTED;
+    chosen = PA_KERNEL_MFMA;
+  } else if (kernel == PA_KERNEL_VALU) {
+    if (!valu) return PA_ERR_UNSUPPORTED;
+    chosen = PA_KERNEL_VALU;
+  } else {
+    if (!mfma && !valu) return PA_ERR_UNSUPPORTED;
+    chosen = mfma ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
+  }
+  const int64_t granule = chosen == PA_KERNEL_MFMA ? kMfmaStep : 1;
+  int64_t part;
+  if (partition_size > 0) {
+    part = round_up(partition_size, granule);
+  } else {
+    // Split only as far as needed to offer kTargetWorkgroups work-groups.
+    const int64_t units = (int64_t)num_seqs * kv_heads;
+    const int64_t splits = units >= kTargetWorkgroups || units == 0
+                               ? 1
+                               : ceil_div(kTargetWorkgroups, units);
+    part = ceil_div(max_seq_len > 0 ? max_seq_len : 1, splits);
+    if (part < 256) part = 256;
+    part = round_up(part, chosen == PA_KERNEL_MFMA ? kMfmaStep : 16);
+  }
+  if (part > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const int64_t parts = max_seq_len > 0 ? ceil_div(max_seq_len, part) : 1;
+  const int64_t grid = parts * (int64_t)num_seqs * kv_heads;
+  if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
+  plan->kernel = chosen;
+  plan->partition = (int32_t)part;
+  plan->partitions = (int32_t)parts;
+  plan->workspace = parts > 1 ? (size_t)num_seqs * num_heads * parts * (head_dim + 2) * 4 : 0;
+  return PA_OK;
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return kAbiVersion; }
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+pa_status pa_block_layout(int64_t tokens, int32_t block_size, int64_t* blocks, int64_t* unused) {
+  if (tokens < 0 || block_size <= 0 || blocks == nullptr || unused == nullptr)
+    return PA_ERR_INVALID_ARG;
+  const int64_t n = tokens / block_size + (tokens % block_size != 0 ? 1 : 0);
+  *blocks = n;
+  *unused = n * block_size - tokens;
+  return PA_OK;
+}
+
+pa_status pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                       int32_t kv_heads, int32_t block_size, int32_t head_dim, int32_t dtype,
+                       void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || kv_heads <= 0 || block_size <= 0 || head_dim <= 0 ||
+      !dtype_ok(dtype))
+    return PA_ERR_INVALID_ARG;
+  const int64_t row_bytes = (int64_t)head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)num_tokens * 2 * kv_heads * (row_bytes / 16) > (int64_t)INT32_MAX * 256)
+    return PA_ERR_INVALID_ARG;
+  return from_hip(pa::launch_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
+                                       num_blocks, kv_heads, block_size, (int)row_bytes,
+                                       (hipStream_t)stream));
+}
+
+pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t max_seq_len, int32_t partition_size,
+                         int32_t dtype, int32_t kernel, int32_t* eff_partition_size,
+                         int32_t* num_partitions, size_t* workspace_bytes) {
+  Plan plan;
+  const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
+                                 max_seq_len, partition_size, dtype, kernel, &plan);
+  if (st != PA_OK) return st;
+  if (eff_partition_size) *eff_partition_size = plan.partition;
+  if (num_partitions) *num_partitions = plan.partitions;
+  if (workspace_bytes) *workspace_bytes = plan.workspace;
+  return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                                 int32_t partition_size, int32_t dtype) {
+  Plan plan;
+  if (make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len,
+                partition_size, dtype, PA_KERNEL_AUTO, &plan) != PA_OK)
+    return 0;
+  return plan.workspace;
+}
+
+pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                       int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, float scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       int32_t dtype, int32_t kernel, void* stream) {
+  Plan plan;
+  const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
+                                 max_seq_len, partition_size, dtype, kernel, &plan);
+  if (st != PA_OK) return st;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  if (plan.workspace > 0 &&
+      (workspace == nullptr || workspace_bytes < plan.workspace || !aligned(workspace, 16)))
+    return PA_ERR_INVALID_ARG;
+
+  pa::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  if (plan.workspace > 0) {
+    p.ws_o = (float*)workspace;
+    p.ws_ml = p.ws_o + (size_t)num_seqs * num_heads * plan.partitions * head_dim;
+  }
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.kv_heads = kv_heads;
+  p.group = num_heads / kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.block_shift = log2i(block_size);
+  p.partition_size = plan.partition;
+  p.num_partitions = plan.partitions;
+  p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == PA_BF16;
+  hipError_t e = plan.kernel == PA_KERNEL_MFMA ? pa::launch_decode_mfma(p, head_dim, s)
+                                               : pa::launch_decode_valu(p, bf16, head_dim, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (plan.partitions > 1) {
+    e = pa::launch_decode_reduce(p, bf16, head_dim, s);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                    int32_t num_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, float scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, int32_t dtype, void* stream) {
+  return pa_decode_ex(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                      max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
+                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype,
+                      PA_KERNEL_AUTO, stream);
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t num_blocks, int32_t kv_heads,
+                         int32_t block_size, int32_t head_dim, int32_t dtype, void* stream) {
+  if (num_pairs < 0 || num_blocks <= 0 || kv_heads <= 0 || block_size <= 0 || head_dim <= 0 ||
+      !dtype_ok(dtype))
+    return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes = (int64_t)kv_heads * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_mapping, 8))
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)num_pairs * 2 * 64 > INT32_MAX) return PA_ERR_INVALID_ARG;
+  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_blocks,
+                                         block_bytes, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal declarations shared by the libpa.so translation units: the decode
+// parameter block, small device helpers and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything a decode launch needs, passed by value as the kernel argument.
+struct DecodeParams {
+  void* out;                    // [B][Hq][D] dtype
+  const void* q;                // [B][Hq][D] dtype
+  const void* k_cache;          // [NB][Hkv][BS][D] dtype
+  const void* v_cache;
+  const int32_t* block_tables;  // [B][max_blocks_per_seq]
+  const int32_t* seq_lens;      // [B]
+  float* ws_o;                  // [B][Hq][num_partitions][D]   unnormalised partial outputs
+  float* ws_ml;                 // [B][Hq][num_partitions][2]   (running max, running sum)
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t kv_heads;
+  int32_t group;                // num_heads / kv_heads
+  int32_t max_blocks_per_seq;
+  int32_t max_seq_len;
+  int32_t num_blocks;
+  int32_t block_size;           // power of two
+  int32_t block_shift;          // log2(block_size)
+  int32_t partition_size;       // tokens per partition
+  int32_t num_partitions;       // grid extent along partitions
+  float scale_log2;             // scale * log2(e): scores kept in base-2 units
+};
+
+// Work-group index -> (kv head, sequence, partition).  Partition-major so that
+// every sequence's first partition is dispatched before any second one, and
+// consecutive work-groups (which the dispatcher spreads over the XCDs) walk
+// the KV heads of one sequence.
+struct WorkItem {
+  int head;
+  int seq;
+  int part;
+};
+
+__device__ inline WorkItem decode_work_item(const DecodeParams& p, int wg) {
+  WorkItem w;
+  w.head = wg % p.kv_heads;
+  const int rest = wg / p.kv_heads;
+  w.seq = rest % p.num_seqs;
+  w.part = rest / p.num_seqs;
+  return w;
+}
+
+__device__ inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// A sequence length the grid and the table can serve.
+__device__ inline bool seq_len_ok(const DecodeParams& p, int len) {
+  return len >= 0 && len <= p.max_seq_len &&
+         (int64_t)len <= ((int64_t)p.max_blocks_per_seq << p.block_shift);
+}
+
+// bfloat16 <-> fp32.  A bf16 is the top half of a binary32.
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);  // v_cvt_pk_bf16_f32: nearest-even
+}
+
+// ---- launchers (return the launch status) --------------------------------
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int64_t* slots, int num_tokens, int64_t num_blocks,
+                            int kv_heads, int block_size, int row_bytes, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
+                              int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
+
+// is_bf16: element type of q/out/caches; head_dim in {64, 128}; group in {1,2,4,8}.
+hipError_t launch_decode_valu(const DecodeParams& p, bool is_bf16, int head_dim,
+                              hipStream_t stream);
+
+// bf16 only; head_dim in {64, 128}; block_size >= 16; group <= 16;
+// partition_size a multiple of 32.
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
+
+// Merges the per-partition partials of sequences with more than one partition.
+hipError_t launch_decode_reduce(const DecodeParams& p, bool is_bf16, int head_dim,
+                                hipStream_t stream);
+
+}  // namespace pa

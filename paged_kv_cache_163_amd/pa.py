@@ -1,0 +1,198 @@
+"""Thin ctypes binding over libpa.so (include/pa.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libpa.so.  Tensors are torch device tensors (torch provides device
+memory and streams); calls are issued on torch's current stream.  Importing
+this module raises ImportError when libpa.so has not been built -- there is no
+fallback implementation.
+
+Tensor layouts (C-contiguous):
+    q, out              [num_seqs, num_heads, head_dim]          float32 | bfloat16
+    k_cache, v_cache    [num_blocks, kv_heads, block_size, head_dim]
+    block_tables        int32 [num_seqs, max_blocks_per_seq]
+    seq_lens            int32 [num_seqs]
+    k_new, v_new        [num_tokens, kv_heads, head_dim]
+    slot_mapping        int64 [num_tokens]
+    block_mapping       int64 [num_pairs, 2]   (src, dst)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m paged_kv_cache_163_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, 1, 2, 3
+PA_F32, PA_BF16 = 0, 1
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+def _sig(name, restype, *argtypes):
+    fn = getattr(_lib, name)
+    fn.restype = restype
+    fn.argtypes = list(argtypes)
+    return fn
+
+
+_abi_version = _sig("pa_abi_version", _i32)
+_status_string = _sig("pa_status_string", ctypes.c_char_p, _i32)
+_block_layout = _sig("pa_block_layout", _i32, _i64, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64))
+_kv_append = _sig("pa_kv_append", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
+_decode_plan = _sig("pa_decode_plan", _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                    ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_sz))
+_workspace_bytes = _sig("pa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32)
+_decode = _sig("pa_decode", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+               _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp)
+_decode_ex = _sig("pa_decode_ex", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                  _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32, _vp)
+_copy_blocks = _sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
+
+EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_append",
+            "pa_decode_plan", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_ex",
+            "pa_copy_blocks"]
+
+
+def abi_version() -> int:
+    return int(_abi_version())
+
+
+def _check(status: int, what: str) -> None:
+    if status == PA_OK:
+        return
+    msg = f"{what}: {_status_string(status).decode()}"
+    if status == PA_ERR_INVALID_ARG:
+        raise ValueError(msg)
+    if status == PA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# --------------------------------------------------------------------------
+
+
+def block_layout(tokens: int, block_size: int) -> tuple[int, int]:
+    """(blocks, unused tail slots) for one unshared sequence; ValueError on bad sizes."""
+    b, u = _i64(), _i64()
+    _check(_block_layout(int(tokens), int(block_size), ctypes.byref(b), ctypes.byref(u)),
+           "block_layout")
+    return int(b.value), int(u.value)
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """Write new tokens' K/V into the cache slots of ``slot_mapping`` (in place)."""
+    dt = _dtype_code(k_cache)
+    for name, t in (("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} dtype {t.dtype} != cache dtype {k_cache.dtype}")
+    nb, hkv, bs, d = k_cache.shape
+    if tuple(v_cache.shape) != (nb, hkv, bs, d):
+        raise ValueError("k_cache and v_cache shapes differ")
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (hkv, d) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [num_tokens, kv_heads, head_dim]")
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != k_new.shape[0]:
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = _kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache", ndim=4),
+                    _dev(v_cache, "v_cache", ndim=4), _dev(slot_mapping, "slot_mapping", torch.int64),
+                    k_new.shape[0], nb, hkv, bs, d, dt, _stream(stream))
+    _check(st, "kv_append")
+
+
+def copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
+    """Copy-on-write: block dst <- block src for each (src, dst) row, both caches."""
+    dt = _dtype_code(k_cache)
+    nb, hkv, bs, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    st = _copy_blocks(_dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+                      _dev(block_mapping, "block_mapping", torch.int64), block_mapping.shape[0],
+                      nb, hkv, bs, d, dt, _stream(stream))
+    _check(st, "copy_blocks")
+
+
+def decode_plan(num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len,
+                partition_size=0, dtype=torch.bfloat16, kernel="auto"):
+    """(partition_size, num_partitions, workspace_bytes) the library will use."""
+    p, n, w = _i32(), _i32(), _sz()
+    code = PA_BF16 if dtype == torch.bfloat16 else PA_F32
+    _check(_decode_plan(num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len,
+                        partition_size, code, KERNELS[kernel], ctypes.byref(p), ctypes.byref(n),
+                        ctypes.byref(w)), "decode_plan")
+    return int(p.value), int(n.value), int(w.value)
+
+
+def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
+           partition_size=0, out=None, workspace=None, kernel="auto", stream=None):
+    """Paged decode attention; returns ``out`` ([num_seqs, num_heads, head_dim], q's dtype).
+
+    ``max_seq_len`` is a host upper bound of ``seq_lens``; when None it is read
+    from the device (one synchronising copy).  ``workspace`` (uint8 device
+    tensor) is allocated when needed and not given.
+    """
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k_cache and v_cache must share a dtype")
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shape does not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must be [num_seqs]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
+    _, _, ws_bytes = decode_plan(B, hq, hkv, d, bs, max_seq_len, partition_size, q.dtype, kernel)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if ws_bytes > 0 and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _decode_ex(_dev(out, "out", ndim=3), _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
+                    _dev(v_cache, "v_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32),
+                    block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
+                    B, hq, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_len, dt,
+                    KERNELS[kernel], _stream(stream))
+    _check(st, "decode")
+    return out

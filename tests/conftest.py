@@ -15,3 +15,12 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="session")
+def built_lib():
+    """Path of libpa.so, building it in-tree only when nothing is built yet."""
+    from paged_kv_cache_163_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    return B.LIB

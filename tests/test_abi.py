@@ -1,0 +1,128 @@
+"""C-ABI surface checks that need no GPU: the library loads, exports every
+function include/pa.h declares, and rejects bad host arguments before any
+HIP call (these calls return before touching the device)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("pa_kv_append", "pa_decode", "pa_copy_blocks"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(built_lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", built_lib], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    lib = ctypes.CDLL(built_lib)
+    for n in declared_functions():
+        assert getattr(lib, n) is not None
+
+
+@pytest.fixture(scope="module")
+def pa(built_lib):
+    from paged_kv_cache_163_amd import pa as binding
+    return binding
+
+
+def test_binding_export_list_matches_header(pa):
+    assert sorted(pa.EXPORTED) == declared_functions()
+    assert pa.abi_version() == 1
+
+
+def test_block_layout_matches_oracle(pa):
+    for bs in (1, 4, 16, 64):
+        for n in list(range(0, 70)) + [850, 2000, 8192]:
+            assert pa.block_layout(n, bs) == oracle.block_layout(n, bs)
+    for tokens, bs in ((-1, 4), (5, 0), (5, -2)):
+        with pytest.raises(ValueError):
+            pa.block_layout(tokens, bs)
+
+
+def test_decode_plan(pa):
+    import torch
+    # 256 x 8 (sequence, head) pairs fill the GPU: no split
+    assert pa.decode_plan(256, 64, 8, 128, 16, 951)[1] == 1
+    # 16 long sequences: split, and a workspace sized B*Hq*parts*(D+2)*4
+    p, n, ws = pa.decode_plan(16, 64, 8, 128, 16, 8192, partition_size=512)
+    assert (p, n) == (512, 16) and ws == 16 * 64 * 16 * 130 * 4
+    p, n, ws = pa.decode_plan(16, 64, 8, 128, 16, 8192)
+    assert n > 1 and p % 32 == 0 and n * p >= 8192
+    # the matrix-core kernel rounds partitions to whole 32-token steps
+    assert pa.decode_plan(4, 8, 2, 64, 16, 100, partition_size=8, dtype=torch.bfloat16,
+                          kernel="mfma")[0] == 32
+    assert pa.decode_plan(4, 8, 2, 64, 4, 100, partition_size=8, dtype=torch.float32)[0] == 8
+    with pytest.raises(NotImplementedError):
+        pa.decode_plan(4, 8, 2, 64, 4, 100, dtype=torch.float32, kernel="mfma")
+    with pytest.raises(NotImplementedError):
+        pa.decode_plan(4, 8, 2, 96, 16, 100)           # head_dim 96 not instantiated
+    with pytest.raises(ValueError):
+        pa.decode_plan(4, 9, 2, 64, 16, 100)           # 9 query heads over 2 KV heads
+
+
+def test_host_validation_rejects_before_launch(built_lib):
+    lib = ctypes.CDLL(built_lib)
+    vp = ctypes.c_void_p
+    fake = vp(4096)  # never dereferenced: every call below fails validation first
+    dec = lib.pa_decode_ex
+    dec.restype = ctypes.c_int32
+    args = dict(out=fake, q=fake, k=fake, v=fake, bt=fake, maxblk=4, sl=fake, maxlen=16, B=2,
+                hq=8, hkv=2, d=64, bs=16, nb=8, scale=0.125, part=0, ws=None, wsb=0, dt=1,
+                kern=0, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return dec(a["out"], a["q"], a["k"], a["v"], a["bt"], ctypes.c_int32(a["maxblk"]),
+                   a["sl"], ctypes.c_int32(a["maxlen"]), ctypes.c_int32(a["B"]),
+                   ctypes.c_int32(a["hq"]), ctypes.c_int32(a["hkv"]), ctypes.c_int32(a["d"]),
+                   ctypes.c_int32(a["bs"]), ctypes.c_int32(a["nb"]), ctypes.c_float(a["scale"]),
+                   ctypes.c_int32(a["part"]), a["ws"], ctypes.c_size_t(a["wsb"]),
+                   ctypes.c_int32(a["dt"]), ctypes.c_int32(a["kern"]), a["stream"])
+
+    INVALID, UNSUPPORTED = 1, 2
+    assert call(hq=9) == INVALID                      # heads do not divide
+    assert call(B=-1) == INVALID
+    assert call(maxlen=-1) == INVALID
+    assert call(nb=0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(dt=7) == INVALID
+    assert call(kern=9) == INVALID
+    assert call(q=None) == INVALID
+    assert call(out=vp(4098)) == INVALID              # not 16-byte aligned
+    assert call(d=96) == UNSUPPORTED
+    assert call(bs=12) == UNSUPPORTED                 # not a power of two
+    assert call(dt=0, kern=2) == UNSUPPORTED          # fp32 has no matrix-core kernel
+    # split needed (16 long sequences at P=512) but no workspace given
+    assert call(B=16, maxlen=8192, maxblk=512, part=512) == INVALID
+    assert call(B=0) == 0                             # nothing to do, nothing launched
+
+    app = lib.pa_kv_append
+    app.restype = ctypes.c_int32
+    i32 = ctypes.c_int32
+    assert app(fake, fake, fake, fake, fake, i32(-1), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID
+    assert app(fake, fake, fake, fake, fake, i32(0), i32(8), i32(2), i32(16), i32(64), i32(1), None) == 0
+    assert app(fake, fake, fake, fake, fake, i32(3), i32(8), i32(2), i32(16), i32(6), i32(1), None) == UNSUPPORTED
+    cp = lib.pa_copy_blocks
+    cp.restype = ctypes.c_int32
+    assert cp(fake, fake, fake, i32(-2), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID
+    assert cp(fake, fake, fake, i32(0), i32(8), i32(2), i32(16), i32(64), i32(1), None) == 0
+    assert cp(fake, fake, None, i32(2), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID

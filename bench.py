@@ -1,0 +1,256 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama70b]
+
+A step is one pass of the whole decode path over one synthetic batch:
+copy-on-write block copies of the batch (if any), KV append of the batch's new
+tokens, then paged decode attention.  Inputs are generated on the host,
+uploaded, and resident in HBM before timing starts.  The KV pools are
+replicated ``--rotate`` times and step i uses copy i mod rotate, so a step
+never finds the previous step's blocks in the 256 MB MALL / L2.
+
+Prints ONE JSON line.  ``value`` is live-KV GB/s of the whole step (live KV
+bytes the decode must read / step time).  ``roofline`` describes the dominant
+kernel (the decode kernel): achieved = live KV bytes per launch / its average
+launch time, timed with HIP events around each decode call on the stream the
+library launches on.  ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/sec, 1 GPU"
+DECODE_KERNEL_SOURCES = ["paged_kv_cache_163_amd/csrc/decode_mfma.hip",
+                         "paged_kv_cache_163_amd/csrc/mfma_step.h",
+                         "paged_kv_cache_163_amd/csrc/pa_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama70b_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama70b",
+                    help="llama70b | shared_prefix | long_context | sweep_b{16,32,64}_d{64,128}")
+    ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled over steps")
+    ap.add_argument("--partition", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "valu"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in DECODE_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
+    None when absent or taken on a different version of the kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle, as it stands, on whole-batch sequences until ~seconds pass."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    except Exception:  # threadpoolctl missing: numpy BLAS thread count unknown
+        threads = 1
+    order = np.random.default_rng(123).permutation(w.num_seqs)
+    done, kv_bytes = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        s = int(order[done % w.num_seqs])
+        oracle.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.scale,
+                            w.block_size, seqs=[s])
+        kv_bytes += int(w.seq_lens[s]) * 2 * w.kv_heads * w.head_dim * w.elem_bytes
+        done += 1
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(kv_bytes / dt / 1e9, 6),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} sequences of the {w.name} batch (random order, seed 123), "
+                   f"{dt:.1f} s single process, numpy float64; "
+                   f"{done / dt:.2f} seqs/s; host has {os.cpu_count()} logical CPUs"),
+        "seqs_per_s": round(done / dt, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the decode path shards by sequence or KV head with no exchange, but no "
+              "multi-GPU run is provided.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_163_amd import build as B
+    from paged_kv_cache_163_amd import workloads as W
+    if not os.path.exists(B.LIB):
+        B.build()
+    from paged_kv_cache_163_amd import pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    w = W.make(args.workload)
+    pools = [(to_dev(w.k_cache), to_dev(w.v_cache)) for _ in range(max(1, args.rotate))]
+    q = to_dev(w.q)
+    bt = to_dev(w.block_tables)
+    lens = to_dev(w.seq_lens)
+    k_new, v_new, slots = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping)
+    pairs = to_dev(w.cow_pairs)
+    out = torch.empty_like(q)
+    plan = pa.decode_plan(w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size,
+                          w.max_seq_len, args.partition, q.dtype, args.kernel)
+    eff_p, nparts, ws_bytes = plan.partition_size, plan.num_partitions, plan.workspace_bytes
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = pools[i % len(pools)]
+        if w.cow_pairs.shape[0]:
+            pa.copy_blocks(kc, vc, pairs)
+        if w.slot_mapping.shape[0]:
+            pa.kv_append(k_new, v_new, kc, vc, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.decode(q, kc, vc, bt, lens, w.scale, max_seq_len=w.max_seq_len,
+                  partition_size=args.partition, out=out, workspace=ws, kernel=args.kernel)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    kv_bytes = W.decode_kv_bytes(w.seq_lens, w.kv_heads, w.head_dim, w.elem_bytes)
+    total_alg = (kv_bytes + 2 * w.q.nbytes + 4 * int(sum(-(-int(n) // w.block_size)
+                                                        for n in w.seq_lens)) + 4 * w.num_seqs)
+    value = kv_bytes / (step_ms * 1e-3) / 1e9
+    kernel_name = f"decode_{plan.kernel}_kernel"
+    split_reduce = plan.kernel != "stream" and nparts > 1
+    dec_avg = float(dec_ms.mean())
+    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
+    traffic = traffic_entry(w.name) if args.partition == 0 and args.kernel == "auto" else None
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs,
+            "num_heads": w.num_heads,
+            "kv_heads": w.kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "num_blocks": w.num_blocks,
+            "mean_seq_len": round(float(w.seq_lens.mean()), 2),
+            "max_seq_len": w.max_seq_len,
+            "appended_tokens": int(w.slot_mapping.shape[0]),
+            "cow_pairs": int(w.cow_pairs.shape[0]),
+            "kernel": plan.kernel,
+            "partition_size": eff_p,
+            "num_partitions" if plan.kernel != "stream" else "workgroups": nparts,
+            "pool_rotation": len(pools),
+            "parallelism": "single GPU",
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),
+        "decode_ms": {"mean": round(dec_avg, 5), "median": round(float(np.median(dec_ms)), 5),
+                      "min": round(float(dec_ms.min()), 5)},
+        "kv_bytes_per_step": kv_bytes,
+        "total_algorithmic_bytes_per_decode": total_alg,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": kernel_name + (" + decode_reduce_kernel" if split_reduce else ""),
+            "bytes_per_launch": kv_bytes,
+            "avg_launch_ms": round(dec_avg, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,7 +15,9 @@
  * ----------------------------------------------
  * Memory.  Every array argument is DEVICE memory owned by the caller, in the
  * layout stated (C order, densely packed), aligned to 16 bytes.  The library
- * allocates nothing, frees nothing and keeps no state between calls.
+ * allocates nothing and frees nothing.  Its only state is a call counter that
+ * tags the stream kernel's tickets and a cached compute-unit count per
+ * device; every call is otherwise independent.
  *
  * One layer's cache.  `k_cache` and `v_cache` are each
  *     [num_blocks][kv_heads][block_size][head_dim]
@@ -62,10 +64,15 @@ typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
 /* Decode kernel selection for pa_decode_ex. */
 typedef enum pa_kernel {
-  PA_KERNEL_AUTO = 0,  /* MFMA kernel when it supports the shape, else VALU  */
-  PA_KERNEL_VALU = 1,  /* vector-ALU kernel: any supported shape and dtype   */
-  PA_KERNEL_MFMA = 2   /* matrix-core kernel: bf16, head_dim 64/128,
-                          block_size 16..256, num_heads/kv_heads <= 16       */
+  PA_KERNEL_AUTO = 0,   /* MFMA when it supports the shape, else VALU        */
+  PA_KERNEL_VALU = 1,   /* vector-ALU split kernel: fp32 or bf16, G <= 8     */
+  PA_KERNEL_MFMA = 2,   /* matrix-core split kernel (+ reduce kernel)        */
+  PA_KERNEL_STREAM = 3  /* matrix-core persistent kernel: a fixed grid of
+                           work-groups shares the batch's work evenly and
+                           merges cut sequences in-kernel (measured slower
+                           than MFMA on MI355X; kept as an option).  MFMA and
+                           STREAM: bf16, head_dim 64/128, block_size 16..256,
+                           num_heads/kv_heads <= 16                          */
 } pa_kernel;
 
 /* Version of this ABI (increments on any signature change). */
@@ -109,27 +116,36 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
                        void* stream);
 
 /*
- * Decode plan: the partition size, the number of partitions and the workspace
- * size that pa_decode/pa_decode_ex will use for these host-side sizes.  All
- * outputs are HOST pointers (any may be NULL).
+ * Decode plan: the kernel, partition size, grid and workspace size that
+ * pa_decode/pa_decode_ex will use for these host-side sizes.  All outputs
+ * are HOST pointers (any may be NULL).
  *
- * Split-sequence decode: each sequence's history is cut into partitions of
- * `partition_size` tokens, one workgroup per (sequence, KV head, partition);
- * when a sequence spans more than one partition, each writes a partial result
- * (running max, running sum, unnormalised output) to the workspace and a
- * second kernel merges them.
- *   partition_size > 0 : used as given by the VALU kernel; rounded up to a
- *                        multiple of 32 tokens by the MFMA kernel;
- *   partition_size = 0 : chosen by the library from num_seqs*kv_heads and
- *                        max_seq_len (no split when there are enough
- *                        (sequence, head) pairs to fill the GPU).
- * workspace bytes = num_seqs*num_heads*num_partitions*(head_dim+2)*4 when
- * num_partitions > 1, else 0.
+ * Split kernels (VALU, MFMA): each sequence's history is cut into partitions
+ * of `partition_size` tokens, one work-group per (sequence, KV head,
+ * partition); a sequence spanning several partitions leaves one partial
+ * result per partition (running max, running sum, unnormalised output) in the
+ * workspace and a reduce kernel merges them.
+ *   partition_size > 0 : used as given by VALU; rounded up to a multiple of
+ *                        32 tokens by MFMA;
+ *   partition_size = 0 : chosen from num_seqs*kv_heads and max_seq_len (no
+ *                        split when there are enough (sequence, head) pairs
+ *                        to fill the GPU).
+ *   workspace = num_seqs*num_heads*num_partitions*(head_dim+2)*4 bytes when
+ *   num_partitions > 1, else 0.  More than 16384 partitions per sequence is
+ *   PA_ERR_UNSUPPORTED.
+ * Stream kernel (STREAM): partition_size is ignored; *eff_partition_size = 0
+ * and *num_partitions = the number of work-groups (2 per compute unit of the
+ * current device, 256 compute units assumed when no device is visible).
+ *   workspace = 8*kv_heads*num_seqs (tickets) + 2*num_workgroups*num_heads/
+ *   kv_heads*(head_dim+2)*4 bytes (partials), 16-byte aligned pieces.  It
+ *   needs no initialising: tickets carry a per-call tag.
+ * Two calls in flight at once must not share a workspace.
  */
 pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t max_seq_len, int32_t partition_size,
-                         int32_t dtype, int32_t kernel, int32_t* eff_partition_size,
-                         int32_t* num_partitions, size_t* workspace_bytes);
+                         int32_t dtype, int32_t kernel, int32_t* kernel_used,
+                         int32_t* eff_partition_size, int32_t* num_partitions,
+                         size_t* workspace_bytes);
 
 /* Workspace bytes pa_decode needs (0 on invalid arguments). */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv_heads,
@@ -153,7 +169,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t kv
  *   max_seq_len   host upper bound of seq_lens (sizes the grid)
  *   scale         multiplies q.k before the softmax (e.g. 1/sqrt(head_dim))
  *   workspace     device scratch of at least pa_decode_workspace_bytes();
- *                 may be NULL when that is 0.  Contents need no initialising.
+ *                 may be NULL when that is 0.  Contents need no initialising;
+ *                 calls in flight at the same time need separate workspaces.
  *
  * out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t][h / G]) * V[t][h / G]
  * with G = num_heads / kv_heads (query head h reads KV head h / G), K[t]/V[t]

@@ -5,8 +5,10 @@
 // o_p = sum exp2(s - m_p) v.  With M = max_p m_p and w_p = exp2(m_p - M):
 //     out = (sum_p w_p o_p) / (sum_p w_p l_p),
 // the same softmax-weighted average as one pass over the whole history.
-// One work-group per (sequence, KV head) covers the G query heads of the
-// group; consecutive threads take consecutive head-dim elements.
+//
+// One 128-thread work-group per (sequence, query head): the weights w_p are
+// computed once into LDS, then each thread sums one head-dim element over the
+// partitions (consecutive threads read consecutive elements of o_p).
 #include <math.h>
 
 #include "pa_internal.h"
@@ -14,54 +16,84 @@
 namespace pa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
+
+__device__ inline float block_max(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmaxf(red[0], red[1]);
+  __syncthreads();
+  return v;
+}
+
+__device__ inline float block_sum(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = red[0] + red[1];
+  __syncthreads();
+  return v;
+}
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p) {
-  const int head = blockIdx.x % p.kv_heads;
-  const int seq = blockIdx.x / p.kv_heads;
+  extern __shared__ float sm_w[];  // [num_partitions] weights w_p
+  __shared__ float red[2];
+  const int hq = blockIdx.x % p.num_heads;
+  const int seq = blockIdx.x / p.num_heads;
   const int len = p.seq_lens[seq];
   if (!seq_len_ok(p, len)) return;  // the partition kernel already wrote NaN
   const int nparts = ceil_div_i(len, p.partition_size);
   if (nparts <= 1) return;          // written directly by the partition kernel
-  const int G = p.group;
-  const int64_t row0 = (int64_t)seq * p.num_heads + (int64_t)head * G;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int g = i / D;
-    const int d = i - g * D;
-    const int64_t slot0 = (row0 + g) * p.num_partitions;
-    const float* ml = p.ws_ml + slot0 * 2;
-    float mx = -INFINITY;
-    for (int q = 0; q < nparts; ++q) mx = fmaxf(mx, ml[2 * q]);
-    float o = 0.f, l = 0.f;
-    for (int q = 0; q < nparts; ++q) {
-      const float wt = exp2f(ml[2 * q] - mx);
-      o += wt * p.ws_o[(slot0 + q) * D + d];
-      l += wt * ml[2 * q + 1];
-    }
-    const float r = o / l;
-    if (BF16)
-      ((uint16_t*)p.out)[(row0 + g) * D + d] = f32_to_bf16(r);
-    else
-      ((float*)p.out)[(row0 + g) * D + d] = r;
+  const int64_t slot0 = ((int64_t)seq * p.num_heads + hq) * p.num_partitions;
+  const float* ml = p.ws_ml + slot0 * 2;
+
+  float mx = -INFINITY;
+  for (int q = threadIdx.x; q < nparts; q += kThreads) mx = fmaxf(mx, ml[2 * q]);
+  mx = block_max(mx, red);
+  float l = 0.f;
+  for (int q = threadIdx.x; q < nparts; q += kThreads) {
+    const float w = exp2f(ml[2 * q] - mx);
+    sm_w[q] = w;
+    l += w * ml[2 * q + 1];
   }
+  l = block_sum(l, red);  // its barriers also publish sm_w
+  const float inv = 1.0f / l;
+  const float* o = p.ws_o + slot0 * D;
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float acc = 0.f;
+    for (int q = 0; q < nparts; ++q) acc += sm_w[q] * o[(int64_t)q * D + d];
+    const float r = acc * inv;
+    const int64_t idx = ((int64_t)seq * p.num_heads + hq) * D + d;
+    if (BF16)
+      ((uint16_t*)p.out)[idx] = f32_to_bf16(r);
+    else
+      ((float*)p.out)[idx] = r;
+  }
+}
+
+template <bool BF16, int D>
+hipError_t launch(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_heads));
+  const size_t lds = (size_t)p.num_partitions * sizeof(float);
+  decode_reduce_kernel<BF16, D><<<grid, kThreads, lds, stream>>>(p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_reduce(const DecodeParams& p, bool is_bf16, int head_dim,
                                 hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.num_seqs * p.kv_heads));
+  if ((size_t)p.num_partitions * sizeof(float) > 64 * 1024) return hipErrorInvalidValue;
   if (is_bf16) {
-    if (head_dim == 64) decode_reduce_kernel<true, 64><<<grid, kThreads, 0, stream>>>(p);
-    else if (head_dim == 128) decode_reduce_kernel<true, 128><<<grid, kThreads, 0, stream>>>(p);
-    else return hipErrorInvalidValue;
+    if (head_dim == 64) return launch<true, 64>(p, stream);
+    if (head_dim == 128) return launch<true, 128>(p, stream);
   } else {
-    if (head_dim == 64) decode_reduce_kernel<false, 64><<<grid, kThreads, 0, stream>>>(p);
-    else if (head_dim == 128) decode_reduce_kernel<false, 128><<<grid, kThreads, 0, stream>>>(p);
-    else return hipErrorInvalidValue;
+    if (head_dim == 64) return launch<false, 64>(p, stream);
+    if (head_dim == 128) return launch<false, 128>(p, stream);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -1,10 +1,15 @@
 // C ABI of libpa.so (declared in include/pa.h): argument checks, decode
-// planning (partition size, grid, workspace) and kernel dispatch.  Every check
-// on host-side arguments runs before the first HIP call, so a rejected call
-// never touches the device.
+// planning (kernel, partition size, grid, workspace) and kernel dispatch.
+// Every check on host-side arguments runs before anything is launched; the
+// only HIP calls before a launch are the device and compute-unit queries of
+// the stream kernel's plan.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#include <time.h>
+#include <unistd.h>
+
+#include <atomic>
 
 #include "../../include/pa.h"
 #include "pa_internal.h"
@@ -16,6 +21,41 @@ constexpr int32_t kAbiVersion = 1;
 // four-wave work-groups per compute unit on a 256-CU MI355X.
 constexpr int64_t kTargetWorkgroups = 1024;
 constexpr int32_t kMfmaStep = 32;  // tokens per MFMA-kernel step
+constexpr int64_t kMaxPartitions = 16384;  // partitions per sequence (split kernels)
+constexpr int32_t kStreamWgsPerCu = 2;   // resident 4-wave work-groups per CU
+constexpr int32_t kDefaultCus = 256;     // MI355X, used when no device is visible
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device (cached per device).
+int32_t device_cus() {
+  static std::atomic<int32_t> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultCus;
+  }
+  int32_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return kDefaultCus;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Per-call tag of the stream kernel's tickets; starts at a per-process value
+// so tickets left in recycled memory by another process do not match.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{(uint32_t)time(nullptr) * 2654435761u ^
+                                       ((uint32_t)getpid() << 16)};
+  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed);
+  return e;
+}
+
+size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -30,9 +70,10 @@ int32_t elem_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
 bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
 
 struct Plan {
-  int32_t kernel;      // PA_KERNEL_VALU or PA_KERNEL_MFMA
-  int32_t partition;   // tokens per partition
-  int32_t partitions;  // grid extent along partitions
+  int32_t kernel;      // PA_KERNEL_VALU, PA_KERNEL_MFMA or PA_KERNEL_STREAM
+  int32_t partition;   // tokens per partition (split kernels), 0 (stream)
+  int32_t partitions;  // grid extent along partitions (split), work-groups (stream)
+  size_t tickets;      // stream: bytes of the ticket array at the workspace start
   size_t workspace;    // bytes
 };
 
@@ -55,22 +96,38 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32
       head_dim <= 0 || block_size <= 0 || max_seq_len < 0 || partition_size < 0 ||
       !dtype_ok(dtype))
     return PA_ERR_INVALID_ARG;
-  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
+  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA &&
+      kernel != PA_KERNEL_STREAM)
     return PA_ERR_INVALID_ARG;
   if (!pow2(block_size) || block_size > 256) return PA_ERR_UNSUPPORTED;
   const int32_t group = num_heads / kv_heads;
   const bool mfma = mfma_supports(dtype, head_dim, group, block_size);
   const bool valu = valu_supports(dtype, head_dim, group, block_size);
+  // The stream kernel indexes its work in int32 steps of 32 tokens.
+  const bool stream_fits =
+      (int64_t)kv_heads * num_seqs * ceil_div(max_seq_len, kMfmaStep) < (int64_t)INT32_MAX;
   int32_t chosen;
-  if (kernel == PA_KERNEL_MFMA) {
+  if (kernel == PA_KERNEL_STREAM) {
+    if (!mfma || !stream_fits) return PA_ERR_UNSUPPORTED;
+    chosen = kernel;
+  } else if (kernel == PA_KERNEL_MFMA) {
     if (!mfma) return PA_ERR_UNSUPPORTED;
-    chosen = PA_KERNEL_MFMA;
+    chosen = kernel;
   } else if (kernel == PA_KERNEL_VALU) {
     if (!valu) return PA_ERR_UNSUPPORTED;
     chosen = PA_KERNEL_VALU;
   } else {
     if (!mfma && !valu) return PA_ERR_UNSUPPORTED;
     chosen = mfma ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
+  }
+  if (chosen == PA_KERNEL_STREAM) {
+    const int64_t wgs = (int64_t)kStreamWgsPerCu * device_cus();
+    plan->kernel = chosen;
+    plan->partition = 0;
+    plan->partitions = (int32_t)wgs;
+    plan->tickets = align16((size_t)kv_heads * num_seqs * 8);
+    plan->workspace = plan->tickets + (size_t)2 * wgs * group * (head_dim + 2) * 4;
+    return PA_OK;
   }
   const int64_t granule = chosen == PA_KERNEL_MFMA ? kMfmaStep : 1;
   int64_t part;
@@ -88,11 +145,13 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32
   }
   if (part > INT32_MAX) return PA_ERR_INVALID_ARG;
   const int64_t parts = max_seq_len > 0 ? ceil_div(max_seq_len, part) : 1;
+  if (parts > kMaxPartitions) return PA_ERR_UNSUPPORTED;  // reduce kernel's LDS weights
   const int64_t grid = parts * (int64_t)num_seqs * kv_heads;
   if (grid > INT32_MAX) return PA_ERR_INVALID_ARG;
   plan->kernel = chosen;
   plan->partition = (int32_t)part;
   plan->partitions = (int32_t)parts;
+  plan->tickets = 0;
   plan->workspace = parts > 1 ? (size_t)num_seqs * num_heads * parts * (head_dim + 2) * 4 : 0;
   return PA_OK;
 }
@@ -147,12 +206,14 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
 
 pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t max_seq_len, int32_t partition_size,
-                         int32_t dtype, int32_t kernel, int32_t* eff_partition_size,
-                         int32_t* num_partitions, size_t* workspace_bytes) {
+                         int32_t dtype, int32_t kernel, int32_t* kernel_used,
+                         int32_t* eff_partition_size, int32_t* num_partitions,
+                         size_t* workspace_bytes) {
   Plan plan;
   const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
                                  max_seq_len, partition_size, dtype, kernel, &plan);
   if (st != PA_OK) return st;
+  if (kernel_used) *kernel_used = plan.kernel;
   if (eff_partition_size) *eff_partition_size = plan.partition;
   if (num_partitions) *num_partitions = plan.partitions;
   if (workspace_bytes) *workspace_bytes = plan.workspace;
@@ -198,7 +259,12 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
   p.v_cache = v_cache;
   p.block_tables = block_tables;
   p.seq_lens = seq_lens;
-  if (plan.workspace > 0) {
+  if (plan.kernel == PA_KERNEL_STREAM) {
+    p.tickets = (uint64_t*)workspace;
+    p.partials = (float*)((char*)workspace + plan.tickets);
+    p.num_workgroups = plan.partitions;
+    p.epoch = next_epoch();
+  } else if (plan.workspace > 0) {
     p.ws_o = (float*)workspace;
     p.ws_ml = p.ws_o + (size_t)num_seqs * num_heads * plan.partitions * head_dim;
   }
@@ -217,6 +283,8 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
 
   const hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dtype == PA_BF16;
+  if (plan.kernel == PA_KERNEL_STREAM)
+    return from_hip(pa::launch_decode_stream(p, head_dim, s));
   hipError_t e = plan.kernel == PA_KERNEL_MFMA ? pa::launch_decode_mfma(p, head_dim, s)
                                                : pa::launch_decode_valu(p, bf16, head_dim, s);
   if (e != hipSuccess) return PA_ERR_HIP;

@@ -17,6 +17,10 @@ struct DecodeParams {
   const int32_t* seq_lens;      // [B]
   float* ws_o;                  // [B][Hq][num_partitions][D]   unnormalised partial outputs
   float* ws_ml;                 // [B][Hq][num_partitions][2]   (running max, running sum)
+  uint64_t* tickets;            // stream kernel: [Hkv][B] epoch-tagged arrival counts
+  float* partials;              // stream kernel: [num_workgroups][2][G*(D+2)]
+  int32_t num_workgroups;       // stream kernel grid
+  uint32_t epoch;               // stream kernel: unique per call
   int32_t num_seqs;
   int32_t num_heads;
   int32_t kv_heads;
@@ -80,6 +84,10 @@ hipError_t launch_decode_valu(const DecodeParams& p, bool is_bf16, int head_dim,
 // bf16 only; head_dim in {64, 128}; block_size >= 16; group <= 16;
 // partition_size a multiple of 32.
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
+
+// Persistent load-balanced kernel: bf16; head_dim in {64, 128}; block_size
+// >= 16; group <= 16; grid = num_workgroups.
+hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
 
 // Merges the per-partition partials of sequences with more than one partition.
 hipError_t launch_decode_reduce(const DecodeParams& p, bool is_bf16, int head_dim,

@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+from typing import NamedTuple
 
 import torch
 
@@ -34,7 +35,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, 1, 2, 3
 PA_F32, PA_BF16 = 0, 1
-KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "stream": 3}
+KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -51,7 +53,8 @@ _status_string = _sig("pa_status_string", ctypes.c_char_p, _i32)
 _block_layout = _sig("pa_block_layout", _i32, _i64, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64))
 _kv_append = _sig("pa_kv_append", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
 _decode_plan = _sig("pa_decode_plan", _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                    ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_sz))
+                    ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                    ctypes.POINTER(_sz))
 _workspace_bytes = _sig("pa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32)
 _decode = _sig("pa_decode", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp)
@@ -148,15 +151,22 @@ def copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
     _check(st, "copy_blocks")
 
 
+class Plan(NamedTuple):
+    kernel: str            # "valu", "mfma" (split partitions) or "stream"
+    partition_size: int    # tokens per partition (0 for "stream")
+    num_partitions: int    # partitions (split kernels) or work-groups ("stream")
+    workspace_bytes: int
+
+
 def decode_plan(num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len,
-                partition_size=0, dtype=torch.bfloat16, kernel="auto"):
-    """(partition_size, num_partitions, workspace_bytes) the library will use."""
-    p, n, w = _i32(), _i32(), _sz()
+                partition_size=0, dtype=torch.bfloat16, kernel="auto") -> Plan:
+    """The kernel, partition size, grid and workspace the library will use."""
+    k, p, n, w = _i32(), _i32(), _i32(), _sz()
     code = PA_BF16 if dtype == torch.bfloat16 else PA_F32
     _check(_decode_plan(num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len,
-                        partition_size, code, KERNELS[kernel], ctypes.byref(p), ctypes.byref(n),
-                        ctypes.byref(w)), "decode_plan")
-    return int(p.value), int(n.value), int(w.value)
+                        partition_size, code, KERNELS[kernel], ctypes.byref(k), ctypes.byref(p),
+                        ctypes.byref(n), ctypes.byref(w)), "decode_plan")
+    return Plan(KERNEL_NAMES[int(k.value)], int(p.value), int(n.value), int(w.value))
 
 
 def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
@@ -180,7 +190,8 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
         raise ValueError("seq_lens must be [num_seqs]")
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
-    _, _, ws_bytes = decode_plan(B, hq, hkv, d, bs, max_seq_len, partition_size, q.dtype, kernel)
+    ws_bytes = decode_plan(B, hq, hkv, d, bs, max_seq_len, partition_size, q.dtype,
+                           kernel).workspace_bytes
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:

@@ -60,23 +60,39 @@ def test_block_layout_matches_oracle(pa):
 
 def test_decode_plan(pa):
     import torch
-    # 256 x 8 (sequence, head) pairs fill the GPU: no split
-    assert pa.decode_plan(256, 64, 8, 128, 16, 951)[1] == 1
-    # 16 long sequences: split, and a workspace sized B*Hq*parts*(D+2)*4
-    p, n, ws = pa.decode_plan(16, 64, 8, 128, 16, 8192, partition_size=512)
-    assert (p, n) == (512, 16) and ws == 16 * 64 * 16 * 130 * 4
-    p, n, ws = pa.decode_plan(16, 64, 8, 128, 16, 8192)
-    assert n > 1 and p % 32 == 0 and n * p >= 8192
-    # the matrix-core kernel rounds partitions to whole 32-token steps
+    # bf16 batches go to the split matrix-core kernel by default
+    assert pa.decode_plan(256, 64, 8, 128, 16, 951).kernel == "mfma"
+    # the persistent stream kernel: 2 work-groups per CU (256 CUs assumed
+    # without a device), tickets + 2 partial slots each
+    plan = pa.decode_plan(256, 64, 8, 128, 16, 951, kernel="stream")
+    assert plan.kernel == "stream" and plan.partition_size == 0
+    nwg = plan.num_partitions
+    assert nwg >= 2 and plan.workspace_bytes == 256 * 8 * 8 + 2 * nwg * 8 * 130 * 4
+    # an explicit partition size selects the split kernel and its workspace
+    plan = pa.decode_plan(16, 64, 8, 128, 16, 8192, partition_size=512)
+    assert plan == ("mfma", 512, 16, 16 * 64 * 16 * 130 * 4)
+    plan = pa.decode_plan(16, 64, 8, 128, 16, 8192, kernel="mfma")
+    assert plan.num_partitions > 1 and plan.partition_size % 32 == 0
+    assert plan.num_partitions * plan.partition_size >= 8192
+    # 256 (sequence, head) pairs fill the GPU for the split kernel: no split
+    assert pa.decode_plan(256, 64, 8, 128, 16, 951, kernel="mfma").num_partitions == 1
+    # the matrix-core split kernel rounds partitions to whole 32-token steps
     assert pa.decode_plan(4, 8, 2, 64, 16, 100, partition_size=8, dtype=torch.bfloat16,
-                          kernel="mfma")[0] == 32
-    assert pa.decode_plan(4, 8, 2, 64, 4, 100, partition_size=8, dtype=torch.float32)[0] == 8
-    with pytest.raises(NotImplementedError):
-        pa.decode_plan(4, 8, 2, 64, 4, 100, dtype=torch.float32, kernel="mfma")
+                          kernel="mfma").partition_size == 32
+    # fp32 runs on the vector-ALU kernel with the partition as given
+    assert pa.decode_plan(4, 8, 2, 64, 4, 100, partition_size=8, dtype=torch.float32) == \
+        ("valu", 8, 13, 4 * 8 * 13 * 66 * 4)
+    assert pa.decode_plan(4, 8, 2, 64, 4, 100, dtype=torch.float32).kernel == "valu"
+    for k in ("mfma", "stream"):
+        with pytest.raises(NotImplementedError):
+            pa.decode_plan(4, 8, 2, 64, 4, 100, dtype=torch.float32, kernel=k)
     with pytest.raises(NotImplementedError):
         pa.decode_plan(4, 8, 2, 96, 16, 100)           # head_dim 96 not instantiated
     with pytest.raises(ValueError):
         pa.decode_plan(4, 9, 2, 64, 16, 100)           # 9 query heads over 2 KV heads
+    # the stream kernel counts steps in int32
+    with pytest.raises(NotImplementedError):
+        pa.decode_plan(65536, 64, 8, 128, 16, 1 << 20, kernel="stream")
 
 
 def test_host_validation_rejects_before_launch(built_lib):
@@ -111,8 +127,12 @@ def test_host_validation_rejects_before_launch(built_lib):
     assert call(d=96) == UNSUPPORTED
     assert call(bs=12) == UNSUPPORTED                 # not a power of two
     assert call(dt=0, kern=2) == UNSUPPORTED          # fp32 has no matrix-core kernel
+    assert call(dt=0, kern=3) == UNSUPPORTED
     # split needed (16 long sequences at P=512) but no workspace given
     assert call(B=16, maxlen=8192, maxblk=512, part=512) == INVALID
+    # the stream kernel always needs its workspace
+    assert call(kern=3) == INVALID
+    assert call(kern=3, ws=vp(4096), wsb=16) == INVALID   # too small
     assert call(B=0) == 0                             # nothing to do, nothing launched
 
     app = lib.pa_kv_append

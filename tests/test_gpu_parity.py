@@ -181,15 +181,48 @@ def test_ragged_bf16_both_kernels(pa, block_size, head_dim):
                 out = decode(pa, d, w, partition_size=partition, kernel=kernel)
                 assert_close(as_f64(out), ref, "bf16",
                              f"b={block_size} d={head_dim} G={hq // hkv} {kernel} P={partition}")
+        out = decode(pa, d, w, kernel="stream")
+        assert_close(as_f64(out), ref, "bf16", f"b={block_size} d={head_dim} G={hq // hkv} stream")
 
 
 @pytest.mark.parametrize("hq,hkv", [(16, 16), (16, 4), (64, 4)])
 def test_group_sizes_mfma(pa, hq, hkv):
-    """G = 1, 4 and 16 query heads per KV head on the matrix-core kernel."""
+    """G = 1, 4 and 16 query heads per KV head on the matrix-core kernels."""
     w = small_bf16([3, 40, 129, 700], 16, 128, hq, hkv, seed=hq * 7 + hkv)
     d = upload(w)
-    out = decode(pa, d, w, kernel="mfma", partition_size=0)
-    assert_close(as_f64(out), oracle_decode(w), "bf16", f"G={hq // hkv}")
+    for kernel in ("mfma", "stream"):
+        out = decode(pa, d, w, kernel=kernel, partition_size=0)
+        assert_close(as_f64(out), oracle_decode(w), "bf16", f"G={hq // hkv} {kernel}")
+
+
+@pytest.mark.parametrize("lens", [
+    [5],                        # fewer steps (8) than work-groups
+    [8192],                     # one unit per head cut across many work-groups
+    [1] * 300 + [4000],         # hundreds of one-step units, then a long one
+    [33, 0, 64, 0, 1, 2500],    # zero-length sequences inside the step space
+], ids=["tiny", "one-long", "many-short", "with-empty"])
+def test_stream_work_split(pa, lens):
+    """The stream kernel's share boundaries: cut units merged through tickets."""
+    w = small_bf16([max(n, 1) for n in lens], 16, 128, 64, 8, seed=len(lens))
+    lens_arr = np.asarray(lens, dtype=np.int32)
+    d = upload(w)
+    d["lens"] = dev(lens_arr)
+    ref = oracle.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, lens_arr, w.scale, 16)
+    plan = pa.decode_plan(w.num_seqs, 64, 8, 128, 16, int(lens_arr.max()), kernel="stream")
+    assert plan.kernel == "stream"
+    # a workspace full of garbage (tickets from no call at all) must not matter
+    ws = torch.randint(0, 255, (plan.workspace_bytes,), dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(3):
+        o = pa.decode(d["q"], d["k"], d["v"], d["bt"], d["lens"], w.scale,
+                      max_seq_len=int(lens_arr.max()), workspace=ws, kernel="stream")
+        torch.cuda.synchronize()
+        outs.append(o.clone())
+    got = as_f64(outs[0])
+    assert_close(got[lens_arr > 0], ref[lens_arr > 0], "bf16", f"stream {lens[:3]}")
+    assert np.all(got[lens_arr == 0] == 0.0)
+    # repeated calls (new ticket tag each time) give the same bytes
+    assert all(torch.equal(outs[0].view(torch.int16), o.view(torch.int16)) for o in outs[1:])
 
 
 def test_edge_lengths_and_bad_contents(pa):
@@ -198,7 +231,7 @@ def test_edge_lengths_and_bad_contents(pa):
     lens = [0, 5, 40, 33]
     w = small_bf16([max(n, 1) for n in lens], 16, 128, 64, 8, seed=3)
     lens_arr = np.asarray(lens, dtype=np.int32)
-    for kernel in ("mfma", "valu"):
+    for kernel in ("stream", "mfma", "valu"):
         d = upload(w)
         d["lens"] = dev(lens_arr)
         bt = w.block_tables.copy()
@@ -270,10 +303,12 @@ def test_llama70b_full(pa):
     # deterministic: the same call gives the same bytes
     again = decode(pa, d, w)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
-    # the vector-ALU kernel agrees with the oracle on a sample too
-    valu = decode(pa, d, w, kernel="valu")
+    # the stream and vector-ALU kernels agree with the oracle too
     seqs = sample_seqs(w, 8, seed=1)
-    assert_close(as_f64(valu)[seqs], oracle_decode(w, kc, vc, seqs=seqs), "bf16", "llama70b valu")
+    for kernel in ("stream", "valu"):
+        o = decode(pa, d, w, kernel=kernel)
+        assert_close(as_f64(o)[seqs], oracle_decode(w, kc, vc, seqs=seqs), "bf16",
+                     f"llama70b {kernel}")
 
 
 def test_shared_prefix_full(pa):
@@ -308,12 +343,15 @@ def test_long_context_full(pa):
     d = upload(w)
     ref = oracle_decode(w, seqs=range(16))
     outs = {}
-    for partition in (512, 0, 1024, 8192):
+    for partition in (512, 1024, 8192, 0):     # split kernel + reduce; 0 = library's choice
         o = decode(pa, d, w, partition_size=partition)
         assert_close(as_f64(o), ref, "bf16", f"long context P={partition}")
         outs[partition] = as_f64(o)
-    # partition size changes rounding only
+    o = decode(pa, d, w, kernel="stream")
+    assert_close(as_f64(o), ref, "bf16", "long context stream")
+    # the partition size and the kernel change rounding only
     assert np.max(np.abs(outs[512] - outs[8192])) < 1e-2
+    assert np.max(np.abs(outs[0] - outs[8192])) < 1e-2
 
 
 @pytest.mark.parametrize("block_size,head_dim", W.SWEEP_CELLS)

@@ -1,9 +1,10 @@
 // Split-partition paged decode on the gfx950 matrix cores (bf16 storage,
 // fp32 accumulation).
 //
-// One work-group of kWaves waves per (sequence, KV head, partition).  The
-// partition is cut into 32-token steps (mfma_step.h); wave w takes steps w,
-// w + kWaves, ...  Loads run one step ahead of the math (two register sets).
+// One work-group of kWaves waves per (sequence, KV head, partition), longest
+// sequences first.  The partition is cut into 32-token steps (mfma_step.h);
+// wave w takes steps w, w + kWaves, ...  Loads run one step ahead of the math
+// (two register sets).
 // At the end the waves merge (m, l, O) through LDS; a single-partition
 // sequence writes its normalised bf16 output directly, otherwise the partial
 // goes to the workspace and decode_reduce.hip merges the partitions.
@@ -24,6 +25,111 @@ using namespace mfma;
 #endif
 constexpr int kWaves = PA_MFMA_WAVES;
 
+// Longest-first work order.  Hardware dispatches work-groups in index order,
+// so giving the low indices to long sequences leaves short ones for the end
+// of the launch and trims its tail (a host-sorted batch ran ~5 % faster).
+// Every work-group derives the same order, a counting sort of the sequences
+// into 256 length bins (longest bin first, index order inside a bin), and
+// takes the sequence at its rank slot.  Wave 0 does the work (its LDS
+// operations are ordered, so no barrier is needed until the hand-off);
+// batches above kRankMaxSeqs keep index order.
+constexpr int kRankMaxSeqs = 4096;
+constexpr int kRankRegs = 8;  // lengths kept in registers per lane (batches <= 512)
+
+// 256 length bins over [0, max_seq_len]; zero and unservable lengths go last.
+__device__ inline int length_bin(int len, int max_len, float bins_per_token) {
+  if (len <= 0 || len > max_len) return 0;
+  return min(255, (int)((float)len * bins_per_token));
+}
+
+struct Ranked {
+  int seq;
+  int len;
+};
+
+__device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_hist,
+                                   int* sm_pick) {
+  const int tid = threadIdx.x;
+  const int B = p.num_seqs;
+  if (B > kRankMaxSeqs) return Ranked{slot, p.seq_lens[slot]};
+  if (tid < 64) {
+    const int lane = tid;
+    const int maxl = p.max_seq_len;
+    const float per_tok = 256.0f / ((float)maxl + 1.0f);
+    int lens[kRankRegs];
+#pragma unroll
+    for (int j = 0; j < kRankRegs; ++j) {
+      const int s = lane + 64 * j;
+      lens[j] = s < B ? p.seq_lens[s] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm_hist[4 * lane + j] = 0;
+#pragma unroll
+    for (int j = 0; j < kRankRegs; ++j)
+      if (lane + 64 * j < B) atomicAdd(&sm_hist[length_bin(lens[j], maxl, per_tok)], 1);
+    for (int s = lane + 64 * kRankRegs; s < B; s += 64)
+      atomicAdd(&sm_hist[length_bin(p.seq_lens[s], maxl, per_tok)], 1);
+    // descending exclusive scan, 4 bins per lane (lane 0 holds the longest)
+    int c[4], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = sm_hist[255 - (4 * lane + j)];
+      tot += c[j];
+    }
+    int incl = tot;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int start = incl - tot, bin = -1, want = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (slot >= start && slot < start + c[j]) {
+        bin = 255 - (4 * lane + j);
+        want = slot - start;
+      }
+      start += c[j];
+    }
+    const uint64_t owner = __ballot(bin >= 0);
+    const int src = __ffsll((unsigned long long)owner) - 1;
+    bin = __shfl(bin, src);
+    want = __shfl(want, src);
+    // the want-th sequence of that bin, in index order (64 sequences per round)
+    int seen = 0, pick = -1, pick_len = 0;
+    for (int j = 0; 64 * j < B; ++j) {
+      int len = -1;
+#pragma unroll
+      for (int r = 0; r < kRankRegs; ++r)
+        if (r == j) len = lens[r];
+      if (j >= kRankRegs && lane + 64 * j < B) len = p.seq_lens[lane + 64 * j];
+      const bool match = lane + 64 * j < B && length_bin(len, maxl, per_tok) == bin;
+      const uint64_t m = __ballot(match);
+      const int n = __popcll(m);
+      if (want < seen + n) {
+        const int before = seen + __popcll(m & ((1ull << lane) - 1));
+        if (match && before == want) {
+          pick = lane + 64 * j;
+          pick_len = len;
+        }
+        break;
+      }
+      seen += n;
+    }
+    const uint64_t found = __ballot(pick >= 0);
+    const int from = __ffsll((unsigned long long)found) - 1;
+    pick = __shfl(pick, from);
+    pick_len = __shfl(pick_len, from);
+    if (lane == 0) {
+      sm_pick[0] = pick;
+      sm_pick[1] = pick_len;
+    }
+  }
+  __syncthreads();
+  // wave-uniform: keep the sequence and its length in scalar registers
+  return Ranked{__builtin_amdgcn_readfirstlane(sm_pick[0]),
+                __builtin_amdgcn_readfirstlane(sm_pick[1])};
+}
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64)
 #if PA_MFMA_MIN_WAVES_PER_EU > 0
@@ -34,15 +140,18 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ float sm_o[kWaves][16][D];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
-
-  const WorkItem w = decode_work_item(p, blockIdx.x);
+  __shared__ int sm_hist[256];
+  __shared__ int sm_pick[2];
+  WorkItem w = decode_work_item(p, blockIdx.x);
+  const Ranked rk = ranked_seq(p, w.seq, sm_hist, sm_pick);
+  w.seq = rk.seq;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15;
   const int q4 = lane >> 4;
   const int G = p.group;
-  const int len = p.seq_lens[w.seq];
+  const int len = rk.len;
   const int64_t out_row0 = (int64_t)w.seq * p.num_heads + (int64_t)w.head * G;
   uint16_t* out = (uint16_t*)p.out;
 

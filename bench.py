@@ -4,7 +4,9 @@
 
 A step is one pass of the whole decode path over one synthetic batch:
 copy-on-write block copies of the batch (if any), KV append of the batch's new
-tokens, then paged decode attention.  Inputs are generated on the host,
+tokens, then paged decode attention.  The append is its own launch
+(pa_kv_append) unless --fused-append moves it into the decode launch
+(pa_decode_append), which measured ~2 us slower per step on the 70B batch.  Inputs are generated on the host,
 uploaded, and resident in HBM before timing starts.  The KV pools are
 replicated ``--rotate`` times and step i uses copy i mod rotate, so a step
 never finds the previous step's blocks in the 256 MB MALL / L2.
@@ -13,7 +15,8 @@ Prints ONE JSON line.  ``value`` is live-KV GB/s of the whole step (live KV
 bytes the decode must read / step time).  ``roofline`` describes the dominant
 kernel (the decode kernel): achieved = live KV bytes per launch / its average
 launch time, timed with HIP events around each decode call on the stream the
-library launches on.  ``cpu_baseline`` times the CPU oracle on a bounded
+library launches on.  The events skip the system-scope cache fence, so timing
+adds no idle gap between launches.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same batch.
 """
 
@@ -47,6 +50,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled over steps")
     ap.add_argument("--partition", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "valu"])
+    ap.add_argument("--fused-append", action="store_true",
+                    help="append inside the decode launch (pa_decode_append)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -72,6 +77,55 @@ def traffic_entry(workload: str):
     if rec.get("kernel_source_hash") != source_hash() or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+class HipTimer:
+    """HIP timing events on torch's own HIP runtime, recorded without the
+    system-scope fence (hipEventDisableSystemFence).  A default event's fence
+    writes back and invalidates the caches and left ~5 us of idle GPU per
+    record between launches; these only take timestamps."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self._c = ctypes
+        self._hip = ctypes.CDLL(path)  # already mapped: the same runtime torch uses
+        self._events = []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def event(self):
+        e = self._c.c_void_p()
+        self._check(self._hip.hipEventCreateWithFlags(self._c.byref(e),
+                                                      self._c.c_uint(self.DISABLE_SYSTEM_FENCE)),
+                    "hipEventCreateWithFlags")
+        self._events.append(e)
+        return e
+
+    def record(self, e, stream):
+        self._check(self._hip.hipEventRecord(e, self._c.c_void_p(stream.cuda_stream)),
+                    "hipEventRecord")
+
+    def elapsed_ms(self, a, b):
+        ms = self._c.c_float()
+        self._check(self._hip.hipEventElapsedTime(self._c.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value
+
+    def close(self):
+        for e in self._events:
+            self._hip.hipEventDestroy(e)
+        self._events = []
 
 
 def cpu_baseline(w, seconds: float):
@@ -149,6 +203,8 @@ def main():
     bt = to_dev(w.block_tables)
     lens = to_dev(w.seq_lens)
     k_new, v_new, slots = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping)
+    fk, fv, fslots = (to_dev(a) for a in W.per_sequence_append(w))
+    fused = w.slot_mapping.shape[0] > 0 and args.fused_append and args.kernel != "stream"
     pairs = to_dev(w.cow_pairs)
     out = torch.empty_like(q)
     plan = pa.decode_plan(w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size,
@@ -161,31 +217,36 @@ def main():
         kc, vc = pools[i % len(pools)]
         if w.cow_pairs.shape[0]:
             pa.copy_blocks(kc, vc, pairs)
-        if w.slot_mapping.shape[0]:
+        if w.slot_mapping.shape[0] and not fused:
             pa.kv_append(k_new, v_new, kc, vc, slots)
         if ev is not None:
-            ev[0].record(stream)
-        pa.decode(q, kc, vc, bt, lens, w.scale, max_seq_len=w.max_seq_len,
-                  partition_size=args.partition, out=out, workspace=ws, kernel=args.kernel)
+            timer.record(ev[0], stream)
+        if fused:   # one launch: the new tokens' append and the decode
+            pa.decode_append(q, kc, vc, fk, fv, fslots, bt, lens, w.scale,
+                             max_seq_len=w.max_seq_len, partition_size=args.partition, out=out,
+                             workspace=ws, kernel=args.kernel)
+        else:
+            pa.decode(q, kc, vc, bt, lens, w.scale, max_seq_len=w.max_seq_len,
+                      partition_size=args.partition, out=out, workspace=ws, kernel=args.kernel)
         if ev is not None:
-            ev[1].record(stream)
+            timer.record(ev[1], stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    timer = HipTimer()
+    evs = [(timer.event(), timer.event()) for _ in range(args.steps)]
+    t_start, t_end = timer.event(), timer.event()
     torch.cuda.synchronize()
-    t_start.record(stream)
+    timer.record(t_start, stream)
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
-    t_end.record(stream)
+    timer.record(t_end, stream)
     torch.cuda.synchronize()
-    step_ms = t_start.elapsed_time(t_end) / args.steps
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    step_ms = timer.elapsed_ms(t_start, t_end) / args.steps
+    dec_ms = np.array([timer.elapsed_ms(a, b) for a, b in evs])
+    timer.close()
 
     kv_bytes = W.decode_kv_bytes(w.seq_lens, w.kv_heads, w.head_dim, w.elem_bytes)
     total_alg = (kv_bytes + 2 * w.q.nbytes + 4 * int(sum(-(-int(n) // w.block_size)
@@ -221,6 +282,7 @@ def main():
             "mean_seq_len": round(float(w.seq_lens.mean()), 2),
             "max_seq_len": w.max_seq_len,
             "appended_tokens": int(w.slot_mapping.shape[0]),
+            "append": "fused into the decode launch" if fused else "pa_kv_append launch",
             "cow_pairs": int(w.cow_pairs.shape[0]),
             "kernel": plan.kernel,
             "partition_size": eff_p,

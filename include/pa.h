@@ -201,6 +201,39 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
                        int32_t dtype, int32_t kernel, void* stream);
 
 /*
+ * Fused decode step: the KV append of one new token per sequence and the
+ * paged decode, in one launch ("How PagedAttention works", section "A strong
+ * answer": each decode step writes the new token's K/V, then attends over the
+ * sequence's blocks).  Same result as
+ *     pa_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, num_seqs, ...)
+ *     pa_decode(out, q, k_cache, v_cache, block_tables, ..., seq_lens, ...)
+ * (bit-identical cache; decode outputs equal up to the rounding of the
+ * chosen kernel), without the second launch.
+ *
+ *   k_new, v_new   [num_seqs][kv_heads][head_dim], dtype: sequence s's new token
+ *   slot_mapping   int64 [num_seqs]: cache slot of sequence s's new token, or
+ *                  < 0 when sequence s appends nothing this step
+ *   seq_lens       lengths AFTER the append; when slot_mapping[s] >= 0 the new
+ *                  token is position seq_lens[s] - 1, and slot_mapping[s] must
+ *                  be that position's slot under the sequence's block table
+ * The decode reads the new token from k_new/v_new, never from the slot being
+ * written, so no work-group reads what another writes.  The slot's block must
+ * not be read by any other sequence in the same call (copy-on-write first).
+ * Other arguments, errors and shapes as pa_decode_ex; kernel PA_KERNEL_STREAM
+ * gives PA_ERR_UNSUPPORTED.  On the 70B-shaped batch one launch measured a
+ * little slower than pa_kv_append + pa_decode (the owning work-group folds
+ * the new token in serially after its step loop).
+ */
+pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                           int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, float scale,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           int32_t dtype, int32_t kernel, void* stream);
+
+/*
  * Copy-on-write block copy: for each (src, dst) pair, copy every KV head and
  * every slot of physical block src into physical block dst, in both caches
  * ("How PagedAttention works", feature table row on beam search and parallel

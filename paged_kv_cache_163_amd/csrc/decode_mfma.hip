@@ -130,7 +130,7 @@ __device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_his
                 __builtin_amdgcn_readfirstlane(sm_pick[1])};
 }
 
-template <int D>
+template <int D, bool kFused>
 __global__ __launch_bounds__(kWaves * 64)
 #if PA_MFMA_MIN_WAVES_PER_EU > 0
 __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES_PER_EU)))
@@ -142,6 +142,7 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ float sm_l[kWaves][16];
   __shared__ int sm_hist[256];
   __shared__ int sm_pick[2];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_new[2 * D * 2];  // fused append
   WorkItem w = decode_work_item(p, blockIdx.x);
   const Ranked rk = ranked_seq(p, w.seq, sm_hist, sm_pick);
   w.seq = rk.seq;
@@ -159,6 +160,7 @@ void decode_mfma_kernel(DecodeParams p) {
     if (w.part == 0) {
       const uint16_t fill = len == 0 ? (uint16_t)0 : (uint16_t)0x7FC0;
       for (int i = tid; i < G * D; i += kWaves * 64) out[out_row0 * D + i] = fill;
+      if (kFused) store_new_token(p, w.seq, w.head, D * 2, tid);
     }
     return;
   }
@@ -166,6 +168,24 @@ void decode_mfma_kernel(DecodeParams p) {
   if (pstart >= len) return;
   const int pend = min(len, pstart + p.partition_size);
   const int nparts = ceil_div_i(len, p.partition_size);
+  // Fused append: the partition that holds the new token (position len - 1,
+  // so the last one) masks it out of the step math and folds it in from the
+  // new row afterwards; partition 0 writes it to its cache slot at the very
+  // end.  Both fetch the slot and the row (wave 0 lanes only) up front, so
+  // neither waits on memory after the loop.
+  constexpr int kRowParts = D / 4;  // 16-byte parts of the K and V rows
+  bool own_new = false;
+  int pend_loop = pend;
+  int64_t new_slot = -1;
+  nt_u32x4 new_part = {0u, 0u, 0u, 0u};
+  if constexpr (kFused) {
+    if ((pend == len || w.part == 0) && tid < kRowParts)
+      new_part = new_row_part(p, w.seq, w.head, D * 2, tid);
+    const NewToken nt = new_token(p, w.seq, w.head, len, D * 2);
+    new_slot = nt.slot;
+    own_new = nt.pos >= pstart && nt.pos < pend;
+    if (own_new) pend_loop = nt.pos;
+  }
 
   // Q^T as the B operand: column r16 = query head h*G + r16, zero when r16 >= G.
   u32x4 qb[kKi];
@@ -191,7 +211,10 @@ void decode_mfma_kernel(DecodeParams p) {
   reset(a);
   bool bad = false;
 
-  // Two register sets, loads one step ahead of the math.
+  // Two register sets, loads one step ahead of the math.  Loads and the loop
+  // run to pend; the math masks from pend_loop, which in fused mode stops one
+  // token short in the owning partition (so no load waits for the new-token
+  // slot, and a wave may meet a step that is wholly masked).
   const int stride = 32 * kWaves;
   int base = pstart + 32 * wave;
   if (base < pend) {
@@ -200,15 +223,20 @@ void decode_mfma_kernel(DecodeParams p) {
     while (true) {
       int next = base + stride;
       if (next < pend) load_step<D>(rb, c, next, r16, q4, bad);
-      compute_step<D>(ra, a, qb, base, pend, p.scale_log2, q4);
+      compute_step<D, kFused>(ra, a, qb, base, pend_loop, p.scale_log2, q4);
       base = next;
       if (base >= pend) break;
       next = base + stride;
       if (next < pend) load_step<D>(ra, c, next, r16, q4, bad);
-      compute_step<D>(rb, a, qb, base, pend, p.scale_log2, q4);
+      compute_step<D, kFused>(rb, a, qb, base, pend_loop, p.scale_log2, q4);
       base = next;
       if (base >= pend) break;
     }
+  }
+  if (kFused && own_new && wave == 0) {
+    if (tid < kRowParts) *(nt_u32x4*)(sm_new + 16 * tid) = new_part;
+    __builtin_amdgcn_wave_barrier();  // one wave: its LDS operations run in order
+    add_token<D>(a, qb, sm_new, sm_new + D * 2, p.scale_log2, r16, q4);
   }
   finish_wave(a, bad);
   stash_wave<D, kWaves>(a, sm_o, sm_m, sm_l, wave, r16, q4, G);
@@ -229,6 +257,7 @@ void decode_mfma_kernel(DecodeParams p) {
       }
     }
   }
+  if (kFused && w.part == 0) store_row_part(p, new_slot, w.head, D * 2, tid, new_part);
 }
 
 }  // namespace
@@ -236,10 +265,15 @@ void decode_mfma_kernel(DecodeParams p) {
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.num_partitions * p.num_seqs * p.kv_heads));
   const dim3 block(kWaves * 64);
-  if (head_dim == 128)
-    decode_mfma_kernel<128><<<grid, block, 0, stream>>>(p);
+  const bool fused = p.new_slots != nullptr;
+  if (head_dim == 128 && fused)
+    decode_mfma_kernel<128, true><<<grid, block, 0, stream>>>(p);
+  else if (head_dim == 128)
+    decode_mfma_kernel<128, false><<<grid, block, 0, stream>>>(p);
+  else if (head_dim == 64 && fused)
+    decode_mfma_kernel<64, true><<<grid, block, 0, stream>>>(p);
   else if (head_dim == 64)
-    decode_mfma_kernel<64><<<grid, block, 0, stream>>>(p);
+    decode_mfma_kernel<64, false><<<grid, block, 0, stream>>>(p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

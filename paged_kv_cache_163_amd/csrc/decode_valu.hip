@@ -77,6 +77,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   const int64_t out_row0 = (int64_t)w.seq * p.num_heads + (int64_t)w.head * G;
 
   if (!seq_len_ok(p, len) || len == 0) {
+    if (w.part == 0) store_new_token(p, w.seq, w.head, D * kElem, lane);
     if (w.part == 0 && grp == 0) {
       const float fill = len == 0 ? 0.0f : __builtin_nanf("");
       for (int g = 0; g < G; ++g)
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     V::unpack(raw, qf[g]);
   }
 
+  const NewToken nt = new_token(p, w.seq, w.head, len, D * kElem);
   float m[G], l[G], acc[G][kVec];
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
@@ -114,9 +116,12 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     }
     const int64_t row = ((((int64_t)phys * p.kv_heads + w.head) << p.block_shift) + (t & bmask));
     const int64_t byte_off = (row * D + sub * kVec) * kElem;
+    const bool fresh = t == nt.pos;  // fused append: the new token comes from its buffer
+    const char* kp = fresh ? nt.krow + sub * kVec * kElem : (const char*)p.k_cache + byte_off;
+    const char* vp = fresh ? nt.vrow + sub * kVec * kElem : (const char*)p.v_cache + byte_off;
     float kf[kVec], vf[kVec];
-    V::unpack(*(const u32x4*)((const char*)p.k_cache + byte_off), kf);
-    V::unpack(*(const u32x4*)((const char*)p.v_cache + byte_off), vf);
+    V::unpack(*(const u32x4*)kp, kf);
+    V::unpack(*(const u32x4*)vp, vf);
     for (int g = 0; g < G; ++g) {
       float dot = 0.0f;
       for (int e = 0; e < kVec; ++e) dot = fmaf(qf[g][e], kf[e], dot);
@@ -154,6 +159,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     }
   }
 
+  // fused append: the cache write comes after every cache read of this group
+  if (w.part == 0) store_new_token(p, w.seq, w.head, D * kElem, lane);
   if (grp != 0) return;
   if (nparts == 1) {
     for (int g = 0; g < G; ++g) {

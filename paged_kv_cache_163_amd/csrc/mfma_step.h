@@ -134,7 +134,10 @@ __device__ inline void load_step(StepRegs<D>& r, const SeqView& c, int base, int
 }
 
 // Scores, online softmax and PV for one loaded step; tokens >= pend masked.
-template <int D>
+// kMayBeEmpty: the step can be wholly masked while the wave has seen no token
+// yet (max still -inf); exponents are then taken against 0 so the state stays
+// empty (l = 0, O = 0) instead of turning NaN.
+template <int D, bool kMayBeEmpty = false>
 __device__ inline void compute_step(StepRegs<D>& r, Acc<D>& a, const u32x4* qb, int base,
                                     int pend, float scale_log2, int q4) {
   constexpr int kKi = D / 32;
@@ -158,13 +161,14 @@ __device__ inline void compute_step(StepRegs<D>& r, Acc<D>& a, const u32x4* qb, 
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(a.m, mx);
-  const float keep = exp2f(a.m - m_new);  // 0 on the first step
+  const float m_ref = (kMayBeEmpty && m_new == -INFINITY) ? 0.f : m_new;
+  const float keep = exp2f(a.m - m_ref);  // 0 on the first step
   u32x4 pb;
   float psum = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const uint32_t lo = f32_to_bf16(exp2f(t[2 * u] - m_new));
-    const uint32_t hi = f32_to_bf16(exp2f(t[2 * u + 1] - m_new));
+    const uint32_t lo = f32_to_bf16(exp2f(t[2 * u] - m_ref));
+    const uint32_t hi = f32_to_bf16(exp2f(t[2 * u + 1] - m_ref));
     pb[u] = lo | (hi << 16);
     psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
   }
@@ -192,6 +196,46 @@ __device__ inline void compute_step(StepRegs<D>& r, Acc<D>& a, const u32x4* qb, 
                        : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
     a.o[jt] = mma(av, pb, a.o[jt]);
+  }
+}
+
+// Fold one extra token into a wave's running state: the fused append's new
+// token, whose K and V rows (bf16, head_dim values each) are staged in LDS.
+// The score is reduced from each lane's share of the head dimension (the same
+// d set its Q operand holds), and the probability is rounded to bf16 exactly
+// as in compute_step, so the result matches reading the token from the cache.
+template <int D>
+__device__ inline void add_token(Acc<D>& a, const u32x4* qb, const unsigned char* krow,
+                                 const unsigned char* vrow, float scale_log2, int r16, int q4) {
+  constexpr int kKi = D / 32;
+  constexpr int kVd = D / 16;
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < kKi; ++i) {
+    const u32x4 kk = *(const u32x4*)(krow + 64 * i + 16 * q4);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      part = fmaf(bf16_lo(qb[i][w]), bf16_lo(kk[w]), part);
+      part = fmaf(bf16_hi(qb[i][w]), bf16_hi(kk[w]), part);
+    }
+  }
+  part += __shfl_xor(part, 16);
+  part += __shfl_xor(part, 32);
+  const float s = part * scale_log2;
+  const float m_new = fmaxf(a.m, s);
+  const float keep = exp2f(a.m - m_new);
+  const uint32_t pbits = f32_to_bf16(exp2f(s - m_new));
+  const float pr = __uint_as_float(pbits << 16);
+  a.l = a.l * keep + (q4 == 0 ? pr : 0.f);  // one share per r16
+  a.m = m_new;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const typename VRow<D>::T vv = *(const typename VRow<D>::T*)(vrow + (kVd * (4 * q4 + r)) * 2);
+#pragma unroll
+    for (int jt = 0; jt < kVd; ++jt) {
+      const float v = (jt & 1) ? bf16_hi(vv[jt >> 1]) : bf16_lo(vv[jt >> 1]);
+      a.o[jt][r] = fmaf(pr, v, a.o[jt][r] * keep);
+    }
   }
 }
 

@@ -160,6 +160,86 @@ pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; 
 
 }  // namespace
 
+static pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                             int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, float scale,
+                             int32_t partition_size, void* workspace, size_t workspace_bytes,
+                             int32_t dtype, int32_t kernel, void* stream, const void* k_new,
+                             const void* v_new, const int64_t* new_slots) {
+  Plan plan;
+  const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
+                                 max_seq_len, partition_size, dtype, kernel, &plan);
+  if (st != PA_OK) return st;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  if (plan.workspace > 0 &&
+      (workspace == nullptr || workspace_bytes < plan.workspace || !aligned(workspace, 16)))
+    return PA_ERR_INVALID_ARG;
+  const bool fused = new_slots != nullptr;
+  if (fused) {
+    if (plan.kernel == PA_KERNEL_STREAM) return PA_ERR_UNSUPPORTED;
+    if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(new_slots, 8))
+      return PA_ERR_INVALID_ARG;
+  }
+
+  pa::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  if (fused) {
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.new_slots = new_slots;
+    p.k_cache_w = (void*)k_cache;
+    p.v_cache_w = (void*)v_cache;
+  }
+  if (plan.kernel == PA_KERNEL_STREAM) {
+    p.tickets = (uint64_t*)workspace;
+    p.partials = (float*)((char*)workspace + plan.tickets);
+    p.num_workgroups = plan.partitions;
+    p.epoch = next_epoch();
+  } else if (plan.workspace > 0) {
+    p.ws_o = (float*)workspace;
+    p.ws_ml = p.ws_o + (size_t)num_seqs * num_heads * plan.partitions * head_dim;
+  }
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.kv_heads = kv_heads;
+  p.group = num_heads / kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.block_shift = log2i(block_size);
+  p.partition_size = plan.partition;
+  p.num_partitions = plan.partitions;
+  p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == PA_BF16;
+  if (plan.kernel == PA_KERNEL_STREAM)
+    return from_hip(pa::launch_decode_stream(p, head_dim, s));
+  hipError_t e = plan.kernel == PA_KERNEL_MFMA ? pa::launch_decode_mfma(p, head_dim, s)
+                                               : pa::launch_decode_valu(p, bf16, head_dim, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (plan.partitions > 1) {
+    e = pa::launch_decode_reduce(p, bf16, head_dim, s);
+    if (e != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+
 extern "C" {
 
 int32_t pa_abi_version(void) { return kAbiVersion; }
@@ -237,62 +317,25 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
                        int32_t block_size, int32_t num_blocks, float scale,
                        int32_t partition_size, void* workspace, size_t workspace_bytes,
                        int32_t dtype, int32_t kernel, void* stream) {
-  Plan plan;
-  const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
-                                 max_seq_len, partition_size, dtype, kernel, &plan);
-  if (st != PA_OK) return st;
-  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
-  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
-    return PA_ERR_INVALID_ARG;
-  if (plan.workspace > 0 &&
-      (workspace == nullptr || workspace_bytes < plan.workspace || !aligned(workspace, 16)))
-    return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                     max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
+                     num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, kernel,
+                     stream, nullptr, nullptr, nullptr);
+}
 
-  pa::DecodeParams p;
-  memset(&p, 0, sizeof(p));
-  p.out = out;
-  p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.block_tables = block_tables;
-  p.seq_lens = seq_lens;
-  if (plan.kernel == PA_KERNEL_STREAM) {
-    p.tickets = (uint64_t*)workspace;
-    p.partials = (float*)((char*)workspace + plan.tickets);
-    p.num_workgroups = plan.partitions;
-    p.epoch = next_epoch();
-  } else if (plan.workspace > 0) {
-    p.ws_o = (float*)workspace;
-    p.ws_ml = p.ws_o + (size_t)num_seqs * num_heads * plan.partitions * head_dim;
-  }
-  p.num_seqs = num_seqs;
-  p.num_heads = num_heads;
-  p.kv_heads = kv_heads;
-  p.group = num_heads / kv_heads;
-  p.max_blocks_per_seq = max_blocks_per_seq;
-  p.max_seq_len = max_seq_len;
-  p.num_blocks = num_blocks;
-  p.block_size = block_size;
-  p.block_shift = log2i(block_size);
-  p.partition_size = plan.partition;
-  p.num_partitions = plan.partitions;
-  p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
-
-  const hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dtype == PA_BF16;
-  if (plan.kernel == PA_KERNEL_STREAM)
-    return from_hip(pa::launch_decode_stream(p, head_dim, s));
-  hipError_t e = plan.kernel == PA_KERNEL_MFMA ? pa::launch_decode_mfma(p, head_dim, s)
-                                               : pa::launch_decode_valu(p, bf16, head_dim, s);
-  if (e != hipSuccess) return PA_ERR_HIP;
-  if (plan.partitions > 1) {
-    e = pa::launch_decode_reduce(p, bf16, head_dim, s);
-    if (e != hipSuccess) return PA_ERR_HIP;
-  }
-  return PA_OK;
+pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                           int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, float scale,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           int32_t dtype, int32_t kernel, void* stream) {
+  if (num_seqs > 0 && slot_mapping == nullptr) return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                     max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
+                     num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, kernel,
+                     stream, k_new, v_new, num_seqs > 0 ? slot_mapping : nullptr);
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -17,6 +17,11 @@ struct DecodeParams {
   const int32_t* seq_lens;      // [B]
   float* ws_o;                  // [B][Hq][num_partitions][D]   unnormalised partial outputs
   float* ws_ml;                 // [B][Hq][num_partitions][2]   (running max, running sum)
+  const void* k_new;            // fused append: [B][Hkv][D] new token per sequence, or null
+  const void* v_new;
+  const int64_t* new_slots;     // fused append: [B] cache slot of each new token (< 0: none)
+  void* k_cache_w;              // fused append: writable views of the caches
+  void* v_cache_w;
   uint64_t* tickets;            // stream kernel: [Hkv][B] epoch-tagged arrival counts
   float* partials;              // stream kernel: [num_workgroups][2][G*(D+2)]
   int32_t num_workgroups;       // stream kernel grid
@@ -60,6 +65,68 @@ __device__ inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 __device__ inline bool seq_len_ok(const DecodeParams& p, int len) {
   return len >= 0 && len <= p.max_seq_len &&
          (int64_t)len <= ((int64_t)p.max_blocks_per_seq << p.block_shift);
+}
+
+// Fused append: the new token of sequence `seq` (position len - 1), if any:
+// its cache slot and the row pointers of its KV head `head`; pos < 0 when
+// there is none (the sequence's slot is negative).
+struct NewToken {
+  int pos;
+  int64_t slot;
+  const char* krow;
+  const char* vrow;
+};
+
+__device__ inline NewToken new_token(const DecodeParams& p, int seq, int head, int len,
+                                     int row_bytes) {
+  NewToken t;
+  t.slot = p.new_slots != nullptr ? p.new_slots[seq] : -1;
+  // Wave-uniform by construction; readfirstlane keeps it (and every bound
+  // derived from it) in scalar registers.
+  t.pos = __builtin_amdgcn_readfirstlane(t.slot >= 0 && len > 0 ? len - 1 : -1);
+  const int64_t off = ((int64_t)seq * p.kv_heads + head) * row_bytes;
+  t.krow = (const char*)p.k_new + off;
+  t.vrow = (const char*)p.v_new + off;
+  return t;
+}
+
+// Fused append: thread `tid` < 2*row_bytes/16 of the caller holds 16 bytes of
+// sequence `seq`'s new row for `head`: threads [0, row_bytes/16) the K row,
+// the rest the V row.  Staged in LDS, the K row comes first and the V row
+// follows it, so thread `tid`'s part goes to byte 16*tid.
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline nt_u32x4 new_row_part(const DecodeParams& p, int seq, int head, int row_bytes,
+                                        int tid) {
+  const int vecs = row_bytes / 16;
+  const bool is_v = tid >= vecs;
+  const int64_t src = ((int64_t)seq * p.kv_heads + head) * row_bytes + (is_v ? tid - vecs : tid) * 16;
+  return *(const nt_u32x4*)((const char*)(is_v ? p.v_new : p.k_new) + src);
+}
+
+// Fused append, cache side: thread `tid`'s part `v` of the new row goes to
+// cache slot `slot` of KV head `head`.  Negative slots and slots outside the
+// pool are not written, as in pa_kv_append.  Kernels call this after their
+// last cache read: a global store that may precede a load makes the compiler
+// give up scalar loads for it (the block-table reads), because the scalar
+// cache is not coherent with vector stores.
+__device__ inline void store_row_part(const DecodeParams& p, int64_t slot, int head,
+                                      int row_bytes, int tid, nt_u32x4 v) {
+  const int vecs = row_bytes / 16;
+  if (tid >= 2 * vecs || slot < 0 || slot >= (int64_t)p.num_blocks * p.block_size) return;
+  const bool is_v = tid >= vecs;
+  const int64_t block = slot >> p.block_shift;
+  const int64_t off = slot & (p.block_size - 1);
+  const int64_t dst = (((block * p.kv_heads + head) << p.block_shift) + off) * row_bytes +
+                      (is_v ? tid - vecs : tid) * 16;
+  *(nt_u32x4*)((char*)(is_v ? p.v_cache_w : p.k_cache_w) + dst) = v;
+}
+
+// The same, reading the slot and the row part itself.
+__device__ inline void store_new_token(const DecodeParams& p, int seq, int head, int row_bytes,
+                                       int tid) {
+  if (p.new_slots == nullptr || tid >= 2 * (row_bytes / 16)) return;
+  store_row_part(p, p.new_slots[seq], head, row_bytes, tid,
+                 new_row_part(p, seq, head, row_bytes, tid));
 }
 
 // bfloat16 <-> fp32.  A bf16 is the top half of a binary32.

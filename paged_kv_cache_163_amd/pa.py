@@ -60,11 +60,14 @@ _decode = _sig("pa_decode", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32
                _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp)
 _decode_ex = _sig("pa_decode_ex", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                   _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32, _vp)
+_decode_append = _sig("pa_decode_append", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32,
+                      _vp)
 _copy_blocks = _sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
 
 EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_append",
             "pa_decode_plan", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_ex",
-            "pa_copy_blocks"]
+            "pa_decode_append", "pa_copy_blocks"]
 
 
 def abi_version() -> int:
@@ -169,14 +172,8 @@ def decode_plan(num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len
     return Plan(KERNEL_NAMES[int(k.value)], int(p.value), int(n.value), int(w.value))
 
 
-def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
-           partition_size=0, out=None, workspace=None, kernel="auto", stream=None):
-    """Paged decode attention; returns ``out`` ([num_seqs, num_heads, head_dim], q's dtype).
-
-    ``max_seq_len`` is a host upper bound of ``seq_lens``; when None it is read
-    from the device (one synchronising copy).  ``workspace`` (uint8 device
-    tensor) is allocated when needed and not given.
-    """
+def _decode_common(q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, partition_size,
+                   out, workspace, kernel):
     dt = _dtype_code(q)
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q, k_cache and v_cache must share a dtype")
@@ -200,10 +197,52 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    common = (_dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+              _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), B, hq, hkv, d, bs, nb)
+    return out, dt, common, ws_ptr, ws_len
+
+
+def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
+           partition_size=0, out=None, workspace=None, kernel="auto", stream=None):
+    """Paged decode attention; returns ``out`` ([num_seqs, num_heads, head_dim], q's dtype).
+
+    ``max_seq_len`` is a host upper bound of ``seq_lens``; when None it is read
+    from the device (one synchronising copy).  ``workspace`` (uint8 device
+    tensor) is allocated when needed and not given.
+    """
+    out, dt, common, ws_ptr, ws_len = _decode_common(
+        q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, partition_size, out,
+        workspace, kernel)
     st = _decode_ex(_dev(out, "out", ndim=3), _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
-                    _dev(v_cache, "v_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32),
-                    block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
-                    B, hq, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_len, dt,
-                    KERNELS[kernel], _stream(stream))
+                    _dev(v_cache, "v_cache", ndim=4), *common, float(scale), int(partition_size),
+                    ws_ptr, ws_len, dt, KERNELS[kernel], _stream(stream))
     _check(st, "decode")
+    return out
+
+
+def decode_append(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_tables, seq_lens, scale,
+                  max_seq_len=None, partition_size=0, out=None, workspace=None, kernel="auto",
+                  stream=None):
+    """Fused decode step: append one new token per sequence, then decode.
+
+    ``k_new``/``v_new`` are [num_seqs, kv_heads, head_dim]; ``slot_mapping``
+    int64 [num_seqs] (< 0: no new token for that sequence); ``seq_lens`` are
+    the lengths after the append.  Same result as ``kv_append`` + ``decode``.
+    """
+    B = q.shape[0]
+    if k_new.shape != (B, k_cache.shape[1], q.shape[2]) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [num_seqs, kv_heads, head_dim]")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise ValueError("k_new/v_new must have q's dtype")
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != B:
+        raise ValueError("slot_mapping must be [num_seqs]")
+    out, dt, common, ws_ptr, ws_len = _decode_common(
+        q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, partition_size, out,
+        workspace, kernel)
+    st = _decode_append(_dev(out, "out", ndim=3), _dev(q, "q", ndim=3),
+                        _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+                        _dev(k_new, "k_new", ndim=3), _dev(v_new, "v_new", ndim=3),
+                        _dev(slot_mapping, "slot_mapping", torch.int64), *common, float(scale),
+                        int(partition_size), ws_ptr, ws_len, dt, KERNELS[kernel], _stream(stream))
+    _check(st, "decode_append")
     return out

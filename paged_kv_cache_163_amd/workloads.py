@@ -161,6 +161,7 @@ class DecodeWorkload:
     k_new: np.ndarray               # [T, Hkv, D] tokens written by the step
     v_new: np.ndarray
     slot_mapping: np.ndarray        # int64 [T]   destination slot per new token
+    append_seq: np.ndarray          # int64 [T]   sequence each new token belongs to
     cow_pairs: np.ndarray           # int64 [n, 2] (src, dst) block copies of the step
     padding_block: int
     refcount: np.ndarray            # int64 [NB]
@@ -181,6 +182,20 @@ class DecodeWorkload:
     @property
     def elem_bytes(self) -> int:
         return 2 if self.dtype == "bf16" else 4
+
+
+def per_sequence_append(w: "DecodeWorkload"):
+    """The step's new tokens laid out one row per sequence, for the fused
+    append+decode call: (k_new [B, Hkv, D], v_new, slot_mapping int64 [B]),
+    zero rows and slot -1 for sequences that append nothing."""
+    B = w.num_seqs
+    k = np.zeros((B,) + w.k_new.shape[1:], dtype=w.k_new.dtype)
+    v = np.zeros_like(k)
+    slots = np.full(B, -1, dtype=np.int64)
+    k[w.append_seq] = w.k_new
+    v[w.append_seq] = w.v_new
+    slots[w.append_seq] = w.slot_mapping
+    return k, v, slots
 
 
 def kv_bytes_per_token(kv_heads: int, head_dim: int, elem_bytes: int, layers: int = 1) -> int:
@@ -300,6 +315,7 @@ def build_private(name: str, pre_lens, *, dtype: str, num_heads: int, kv_heads: 
         block_tables=_pack_tables(tables, padding),
         seq_lens=seq_lens.astype(np.int32), pre_lens=pre_lens.astype(np.int32),
         k_new=k_new, v_new=v_new, slot_mapping=slots,
+        append_seq=np.arange(slots.shape[0], dtype=np.int64),
         cow_pairs=np.zeros((0, 2), dtype=np.int64), padding_block=int(padding),
         refcount=pool.refcount.copy(), meta=dict(meta or {}))
 
@@ -407,6 +423,7 @@ def shared_prefix(seed: int = 0, num_seqs: int = 200, num_beams: int = 16,
         block_tables=_pack_tables(tables, padding),
         seq_lens=seq_lens.astype(np.int32), pre_lens=pre_all.astype(np.int32),
         k_new=k_new, v_new=v_new, slot_mapping=np.asarray(slots, dtype=np.int64),
+        append_seq=np.arange(num_seqs, num_seqs + num_beams, dtype=np.int64),
         cow_pairs=np.asarray(pairs, dtype=np.int64).reshape(-1, 2),
         padding_block=int(padding), refcount=pool.refcount.copy(),
         meta={"parent": parent, "shared_blocks": shared, "prefix_blocks": prefix_blocks,

@@ -141,6 +141,17 @@ def test_host_validation_rejects_before_launch(built_lib):
     assert app(fake, fake, fake, fake, fake, i32(-1), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID
     assert app(fake, fake, fake, fake, fake, i32(0), i32(8), i32(2), i32(16), i32(64), i32(1), None) == 0
     assert app(fake, fake, fake, fake, fake, i32(3), i32(8), i32(2), i32(16), i32(6), i32(1), None) == UNSUPPORTED
+    fa = lib.pa_decode_append
+    fa.restype = ctypes.c_int32
+    none = None
+    # fused call without a slot mapping
+    assert fa(fake, fake, fake, fake, fake, fake, none, fake, i32(4), fake, i32(16), i32(2),
+              i32(8), i32(2), i32(64), i32(16), i32(8), ctypes.c_float(0.1), i32(0), fake,
+              ctypes.c_size_t(1 << 20), i32(1), i32(0), none) == INVALID
+    # fused call on the stream kernel
+    assert fa(fake, fake, fake, fake, fake, fake, fake, fake, i32(4), fake, i32(16), i32(2),
+              i32(8), i32(2), i32(64), i32(16), i32(8), ctypes.c_float(0.1), i32(0), fake,
+              ctypes.c_size_t(1 << 26), i32(1), i32(3), none) == UNSUPPORTED
     cp = lib.pa_copy_blocks
     cp.restype = ctypes.c_int32
     assert cp(fake, fake, fake, i32(-2), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID

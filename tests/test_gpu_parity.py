@@ -358,3 +358,70 @@ def test_long_context_full(pa):
 def test_sweep_full(pa, block_size, head_dim):
     w = W.sweep(block_size, head_dim)
     _full_step_and_decode(pa, w, nsample=16)
+
+
+# --------------------------------------------------------------------------
+# fused decode step: pa_decode_append == pa_kv_append + pa_decode
+# --------------------------------------------------------------------------
+
+FUSED_PRE = [1, 15, 16, 17, 31, 32, 33, 64, 95, 96, 97, 511, 512, 513]
+
+
+def _fused_case(block_size, head_dim, skip=(2, 5), seed=9):
+    nb = sum(-(-(n + 1) // block_size) for n in FUSED_PRE) + 8
+    w = W.build_private("fused", FUSED_PRE, dtype="bf16", num_heads=64, kv_heads=8,
+                        head_dim=head_dim, block_size=block_size, num_blocks=nb, append=True,
+                        seed=seed)
+    for s in skip:                       # these sequences append nothing this step
+        w.slot_mapping[s] = -1
+        w.seq_lens[s] = w.pre_lens[s]
+    return w
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+@pytest.mark.parametrize("block_size,head_dim", [(16, 128), (32, 64), (64, 128)])
+def test_fused_append_decode(pa, kernel, block_size, head_dim):
+    w = _fused_case(block_size, head_dim)
+    kc, vc = oracle_step(w)
+    ref = oracle_decode(w, kc, vc)
+    k, v, slots = W.per_sequence_append(w)
+    for partition in (32, 64, 0):        # P=32 leaves some new tokens alone in a partition
+        d = upload(w)
+        out = pa.decode_append(d["q"], d["k"], d["v"], dev(k), dev(v), dev(slots), d["bt"],
+                               d["lens"], w.scale, max_seq_len=w.max_seq_len,
+                               partition_size=partition, kernel=kernel)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(d["k"]), kc) and np.array_equal(host(d["v"]), vc)
+        assert_close(as_f64(out), ref, "bf16", f"fused {kernel} b={block_size} d={head_dim} P={partition}")
+
+
+def test_fused_append_decode_fp32_tiny(pa):
+    w = W.tiny()
+    kc, vc = oracle_step(w)
+    ref = oracle_decode(w, kc, vc)
+    k, v, slots = W.per_sequence_append(w)
+    for partition in (8, 0):
+        d = upload(w)
+        out = pa.decode_append(d["q"], d["k"], d["v"], dev(k), dev(v), dev(slots), d["bt"],
+                               d["lens"], w.scale, max_seq_len=w.max_seq_len,
+                               partition_size=partition)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(d["k"]).view(np.uint32), kc.view(np.uint32))
+        assert_close(as_f64(out), ref, "f32", f"fused fp32 P={partition}")
+
+
+def test_fused_append_decode_full_size(pa):
+    """The benchmark's fused step on the 70B-shaped batch."""
+    w = W.llama70b()
+    kc, vc = oracle_step(w)
+    k, v, slots = W.per_sequence_append(w)
+    d = upload(w)
+    out = pa.decode_append(d["q"], d["k"], d["v"], dev(k), dev(v), dev(slots), d["bt"], d["lens"],
+                           w.scale, max_seq_len=w.max_seq_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(d["k"]), kc) and np.array_equal(host(d["v"]), vc)
+    seqs = sample_seqs(w, 24)
+    assert_close(as_f64(out)[seqs], oracle_decode(w, kc, vc, seqs=seqs), "bf16", "fused llama70b")
+    with pytest.raises(NotImplementedError):
+        pa.decode_append(d["q"], d["k"], d["v"], dev(k), dev(v), dev(slots), d["bt"], d["lens"],
+                         w.scale, max_seq_len=w.max_seq_len, kernel="stream")

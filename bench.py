@@ -252,11 +252,13 @@ def main():
     total_alg = (kv_bytes + 2 * w.q.nbytes + 4 * int(sum(-(-int(n) // w.block_size)
                                                         for n in w.seq_lens)) + 4 * w.num_seqs)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
-    kernel_name = f"decode_{plan.kernel}_kernel"
+    kernel_name = f"decode_{plan.kernel}_kernel" + (" (fused append)" if fused else "")
     split_reduce = plan.kernel != "stream" and nparts > 1
     dec_avg = float(dec_ms.mean())
     achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
-    traffic = traffic_entry(w.name) if args.partition == 0 and args.kernel == "auto" else None
+    # the stored counter record is for the plain decode kernel at the default plan
+    plain = args.partition == 0 and args.kernel == "auto" and not fused
+    traffic = traffic_entry(w.name) if plain else None
 
     line = {
         "metric": METRIC,

@@ -1,4 +1,4 @@
-"""CPU oracle for paged decode attention. TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for paged decode (and chunked prefill) attention. TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import, call or execute anything in this package.  The
@@ -28,12 +28,15 @@ from .paged_attention import (  # noqa: F401
     attend,
     bf16_bits_to_f64,
     block_layout,
+    chunk_positions,
     contiguous_decode,
     copy_blocks,
     gather_history,
     gather_history_vectorised,
     kv_append,
     paged_decode,
+    paged_prefill,
     to_f64,
     translate,
+    visible_prefix,
 )

@@ -189,6 +189,67 @@ def contiguous_decode(q, keys_per_seq, values_per_seq, scale: float) -> np.ndarr
 
 
 # --------------------------------------------------------------------------
+# Prefill: a chunk of queries per sequence, causal
+# --------------------------------------------------------------------------
+
+def chunk_positions(seq_len: int, query_len: int) -> np.ndarray:
+    """Positions of a sequence's prefill queries.
+
+    The chunk's keys and values are already in the cache, so its queries are
+    the last ``query_len`` of the ``seq_len`` cached positions: L - n, ...,
+    L - 1 (a whole prompt when n = L; a later chunk after a cached prefix
+    when n < L, the prefix-reuse case of "How PagedAttention works", section
+    "A strong answer").
+    """
+    if query_len < 0 or query_len > seq_len:
+        raise ValueError(f"chunk of {query_len} queries in a sequence of {seq_len}")
+    return np.arange(seq_len - query_len, seq_len, dtype=np.int64)
+
+
+def visible_prefix(position: int, seq_len: int) -> int:
+    """How many positions the query at ``position`` attends: [0, position].
+
+    lihaoran.work explainer, section "A block table maps logical order to
+    physical storage": full causal attention covers the visible history, so
+    a query sees itself and every earlier position, never a later one.
+    """
+    return position + 1
+
+
+def paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale: float,
+                  block_size: int, rows=None, literal: bool = False) -> np.ndarray:
+    """Causal attention of each sequence's chunk of queries over its paged history.
+
+    ``q`` ``[num_queries, num_heads, head_dim]`` holds the sequences' chunks
+    one after another: sequence s owns rows [start_s, start_s + query_lens[s])
+    with start_s the sum of the earlier query_lens.  Its history is gathered
+    through its block table as in decode; the query at position p
+    (:func:`chunk_positions`) then attends the first :func:`visible_prefix`
+    positions with :func:`attend`.  ``rows`` limits the work to the listed
+    global query rows.  Returns float64 ``[len(rows), num_heads, head_dim]``.
+    """
+    q = np.asarray(q)
+    query_lens = np.asarray(query_lens, dtype=np.int64)
+    starts = np.concatenate([[0], np.cumsum(query_lens)])
+    if rows is None:
+        rows = range(int(starts[-1]))
+    rows = [int(r) for r in rows]
+    gather = gather_history if literal else gather_history_vectorised
+    histories = {}
+    out = np.empty((len(rows), q.shape[1], q.shape[2]), dtype=np.float64)
+    for i, r in enumerate(rows):
+        s = int(np.searchsorted(starts, r, side="right")) - 1
+        seq_len = int(seq_lens[s])
+        if s not in histories:
+            histories[s] = gather(k_cache, v_cache, block_tables[s], seq_len, block_size)
+        keys, values = histories[s]
+        position = int(chunk_positions(seq_len, int(query_lens[s]))[r - int(starts[s])])
+        seen = visible_prefix(position, seq_len)
+        out[i] = attend(to_f64(q[r]), keys[:seen], values[:seen], scale)
+    return out
+
+
+# --------------------------------------------------------------------------
 # Cache writes
 # --------------------------------------------------------------------------
 

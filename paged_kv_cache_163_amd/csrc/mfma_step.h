@@ -101,10 +101,20 @@ __device__ inline void reset(Acc<D>& a) {
 // Issue the loads of the step starting at token `base` (a multiple of 32).
 // Tiles wholly past the sequence re-read its last live block (masked later),
 // so every load stays inside the caches.  A table entry outside the pool sets
-// `bad` and reads block 0 instead.  K/V are read once per launch, so the
-// loads are non-temporal: they do not displace reusable lines from L2/MALL
-// (measured ~10 % faster on the 70B-shaped batch).
-template <int D>
+// `bad` and reads block 0 instead.  Decode reads K/V once per launch, so by
+// default (kStream) the loads are non-temporal: they do not displace reusable
+// lines from L2/MALL (measured ~10 % faster on the 70B-shaped batch).
+// Prefill re-reads every tile from several waves and work-groups and wants
+// them cached (kStream = false).
+template <typename T, bool kStream>
+__device__ inline T load16(const T* p) {
+  if constexpr (kStream)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <int D, bool kStream = true>
 __device__ inline void load_step(StepRegs<D>& r, const SeqView& c, int base, int r16, int q4,
                                  bool& bad) {
   constexpr int kRow = D * 2;  // bytes per token row
@@ -125,10 +135,10 @@ __device__ inline void load_step(StepRegs<D>& r, const SeqView& c, int base, int
     const uint32_t voff = (uint32_t)((4 * q4) * kRow + r16 * (D / 16) * 2);
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
-      r.k[kt][i] = __builtin_nontemporal_load((const u32x4*)(kt_base + (koff + 64u * i)));
+      r.k[kt][i] = load16<u32x4, kStream>((const u32x4*)(kt_base + (koff + 64u * i)));
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      r.v[4 * kt + e] = __builtin_nontemporal_load(
+      r.v[4 * kt + e] = load16<typename VRow<D>::T, kStream>(
           (const typename VRow<D>::T*)(vt_base + (voff + (uint32_t)(e * kRow))));
   }
 }

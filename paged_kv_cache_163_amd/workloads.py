@@ -431,6 +431,150 @@ def shared_prefix(seed: int = 0, num_seqs: int = 200, num_beams: int = 16,
               "tails": "U{1..400}"})
 
 
+# --------------------------------------------------------------------------
+# prefill workloads: a chunk of queries per sequence, its K/V already cached
+# --------------------------------------------------------------------------
+
+@dataclass
+class PrefillWorkload:
+    name: str
+    dtype: str
+    num_heads: int
+    kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    q: np.ndarray                   # [T, Hq, D]: sequence s's chunk is rows query_start[s]..
+    k_cache: np.ndarray             # [NB, Hkv, b, D] holding every position, chunk included
+    v_cache: np.ndarray
+    block_tables: np.ndarray        # int32 [B, max_blocks_per_seq]
+    seq_lens: np.ndarray            # int32 [B] cached positions after the chunk's append
+    query_lens: np.ndarray          # int32 [B] chunk length (the last query_lens[s] positions)
+    padding_block: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_queries(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def query_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.query_lens)]).astype(np.int32)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.size else 0
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.query_lens.size else 0
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+
+def _draw_rows(seed: int, kind: int, shape, dtype: str, rows_per_stream: int = 256) -> np.ndarray:
+    """_draw over the leading axis in chunks of rows, chunk i from its own stream
+    default_rng([seed, kind, i]), filled in parallel (same result for any
+    thread count)."""
+    out = np.empty(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    chunks = range(_ceil_div(shape[0], rows_per_stream))
+
+    def fill(i):
+        lo = i * rows_per_stream
+        hi = min(shape[0], lo + rows_per_stream)
+        out[lo:hi] = _draw(_stream(seed, kind, i), (hi - lo,) + tuple(shape[1:]), dtype)
+
+    with ThreadPoolExecutor(_FILL_THREADS) as ex:
+        list(ex.map(fill, chunks))
+    return out
+
+
+def prefill_flops(seq_lens, query_lens, num_heads: int, head_dim: int) -> int:
+    """Multiply-adds x 2 of causal prefill: a query at position p scores p + 1
+    keys (2*D flops each) and sums as many V rows (2*D), for every query head."""
+    total = 0
+    for n_ctx, n_q in zip(np.asarray(seq_lens, dtype=np.int64), np.asarray(query_lens, dtype=np.int64)):
+        first = int(n_ctx - n_q) + 1                 # keys seen by the chunk's first query
+        last = int(n_ctx)
+        total += (first + last) * int(n_q) // 2      # sum of an arithmetic run
+    return 4 * head_dim * num_heads * total
+
+
+def build_prefill(name: str, seq_lens, query_lens, *, dtype: str, num_heads: int, kv_heads: int,
+                  head_dim: int, block_size: int, num_blocks: int, seed: int = 0,
+                  meta: dict | None = None) -> PrefillWorkload:
+    """Private blocks holding every position (build_private with no append), and
+    the chunks' queries, 256 rows per stream default_rng([seed, 13, i])."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    query_lens = np.asarray(query_lens, dtype=np.int64)
+    if np.any(query_lens > seq_lens) or np.any(query_lens < 0):
+        raise ValueError("a chunk cannot be longer than its sequence")
+    base = build_private(name, seq_lens, dtype=dtype, num_heads=num_heads, kv_heads=kv_heads,
+                         head_dim=head_dim, block_size=block_size, num_blocks=num_blocks,
+                         append=False, seed=seed)
+    q = _draw_rows(seed, 13, (int(query_lens.sum()), num_heads, head_dim), dtype)
+    return PrefillWorkload(
+        name=name, dtype=dtype, num_heads=num_heads, kv_heads=kv_heads, head_dim=head_dim,
+        block_size=block_size, num_blocks=num_blocks, scale=base.scale, q=q,
+        k_cache=base.k_cache, v_cache=base.v_cache, block_tables=base.block_tables,
+        seq_lens=seq_lens.astype(np.int32), query_lens=query_lens.astype(np.int32),
+        padding_block=base.padding_block, meta=dict(meta or {}))
+
+
+def prefill_tiny(seed: int = 0, head_dim: int = 64, block_size: int = 16,
+                 group: int = 4) -> PrefillWorkload:
+    """Ragged chunks: whole prompts, chunks after a cached prefix, single
+    queries, a sequence with no chunk.  bf16, 2 KV heads."""
+    seq_lens = [37, 16, 5, 300, 64, 1, 40, 129]
+    query_lens = [37, 9, 5, 70, 1, 1, 0, 129]
+    need = sum(_ceil_div(n, block_size) for n in seq_lens)
+    return build_prefill("prefill_tiny", seq_lens, query_lens, dtype="bf16",
+                         num_heads=2 * group, kv_heads=2, head_dim=head_dim,
+                         block_size=block_size, num_blocks=need + 8, seed=seed)
+
+
+def prefill_llama70b(seed: int = 0, num_seqs: int = 32) -> PrefillWorkload:
+    """Whole-prompt prefill of 32 chat prompts of U{500..700} tokens (the
+    pages' 600-token prompt) on the Llama-3.1-70B layer shape."""
+    rng = np.random.default_rng([seed, 17])
+    prompt = rng.integers(500, 700, size=num_seqs, endpoint=True)
+    need = int(sum(_ceil_div(int(n), 16) for n in prompt))
+    return build_prefill("prefill_llama70b", prompt, prompt, dtype="bf16", num_heads=64,
+                         kv_heads=8, head_dim=128, block_size=16, num_blocks=need + 64,
+                         seed=seed, meta={"prompt": "U{500..700}", "chunk": "whole prompt"})
+
+
+def prefill_chunked(seed: int = 0, num_seqs: int = 32, chunk: int = 256) -> PrefillWorkload:
+    """A 256-token chunk after a cached prefix of U{500..1500} tokens per
+    sequence (a prompt continued over reused prefix blocks), 70B layer shape."""
+    rng = np.random.default_rng([seed, 19])
+    prefix = rng.integers(500, 1500, size=num_seqs, endpoint=True)
+    seq_lens = prefix + chunk
+    need = int(sum(_ceil_div(int(n), 16) for n in seq_lens))
+    return build_prefill("prefill_chunked", seq_lens, [chunk] * num_seqs, dtype="bf16",
+                         num_heads=64, kv_heads=8, head_dim=128, block_size=16,
+                         num_blocks=need + 64, seed=seed,
+                         meta={"prefix": "U{500..1500}", "chunk": chunk})
+
+
+PREFILL_WORKLOADS = {
+    "prefill_tiny": prefill_tiny,
+    "prefill_llama70b": prefill_llama70b,
+    "prefill_chunked": prefill_chunked,
+}
+
+
 WORKLOADS = {
     "tiny": tiny,
     "llama70b": llama70b,

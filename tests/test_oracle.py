@@ -336,12 +336,87 @@ def pin_bf16_decode():
     return special[0] == np.inf and special[1] == -np.inf and np.isnan(special[2])
 
 
+# ---- chunked prefill -------------------------------------------------------
+
+def _sdpa_causal(q_full, keys, values, scale, group):
+    """torch's CPU scaled_dot_product_attention in fp64 with a causal mask:
+    row i of ``q_full`` [L, Hq, D] attends keys 0..i of ``keys`` [L, Hkv, D]."""
+    import torch
+    qt = torch.from_numpy(q_full).permute(1, 0, 2)
+    kt = torch.from_numpy(keys).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    vt = torch.from_numpy(values).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt.contiguous(), kt.contiguous(), vt.contiguous(), is_causal=True, scale=scale)
+    return out.permute(1, 0, 2).numpy()
+
+
+def pin_prefill_single_query_is_decode():
+    """A one-query chunk is the decode query at the sequence's last position."""
+    rng = np.random.default_rng(21)
+    lens = [7, 1, 20]
+    q, kc, vc, tables, _, _ = _random_paged_batch(rng, lens, 8, 2, 16, 4)
+    out = oracle.paged_prefill(q, kc, vc, tables, lens, [1, 1, 1], 0.3, 4)
+    return np.array_equal(out, oracle.paged_decode(q, kc, vc, tables, lens, 0.3, 4))
+
+
+def pin_prefill_torch_sdpa_causal():
+    """Whole prompts (chunk = sequence) against torch's causal attention."""
+    rng = np.random.default_rng(22)
+    lens = [13, 1, 33]
+    hq, hkv, d, bs = 8, 2, 16, 4
+    _, kc, vc, tables, keys, values = _random_paged_batch(rng, lens, hq, hkv, d, bs)
+    qs = [rng.standard_normal((n, hq, d)) for n in lens]
+    out = oracle.paged_prefill(np.concatenate(qs), kc, vc, tables, lens, lens, 0.25, bs)
+    ref = np.concatenate([_sdpa_causal(qs[s], keys[s], values[s], 0.25, hq // hkv)
+                          for s in range(len(lens))])
+    return np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_prefill_chunk_rows_of_full():
+    """A chunk after a cached prefix gives the matching rows of whole-prompt
+    causal attention (torch) over the full sequence."""
+    rng = np.random.default_rng(23)
+    lens, nq = [17, 9, 30], [5, 9, 1]
+    hq, hkv, d, bs = 4, 4, 8, 4
+    _, kc, vc, tables, keys, values = _random_paged_batch(rng, lens, hq, hkv, d, bs)
+    q_full = [rng.standard_normal((n, hq, d)) for n in lens]
+    q = np.concatenate([q_full[s][lens[s] - nq[s]:] for s in range(3)])
+    out = oracle.paged_prefill(q, kc, vc, tables, lens, nq, 0.25, bs)
+    ref = np.concatenate([_sdpa_causal(q_full[s], keys[s], values[s], 0.25, 1)[lens[s] - nq[s]:]
+                          for s in range(3)])
+    return np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_prefill_future_keys_ignored():
+    """NaN written into every position after a query's own leaves that
+    query's output unchanged (causality), and positions before it matter."""
+    rng = np.random.default_rng(24)
+    lens = [12]
+    q, kc, vc, tables, _, _ = _random_paged_batch(rng, lens, 4, 2, 8, 4)
+    qc = rng.standard_normal((12, 4, 8))
+    base = oracle.paged_prefill(qc, kc, vc, tables, lens, [12], 0.5, 4)
+    for p in (0, 5, 11):
+        kp, vp = kc.copy(), vc.copy()
+        for t in range(p + 1, 12):
+            blk, off = oracle.translate(tables[0], t, 4)
+            kp[blk, :, off, :] = np.nan
+            vp[blk, :, off, :] = np.nan
+        row = oracle.paged_prefill(qc, kp, vp, tables, lens, [12], 0.5, 4, rows=[p])
+        if not np.array_equal(row[0], base[p]):
+            return False
+    if np.allclose(base[5], base[6]):
+        return False
+    return True
+
+
 ALL_PINS = [
     pin_block_layout_golden, pin_block_layout_bounds, pin_translation_golden,
     pin_paged_equals_contiguous, pin_single_token, pin_equal_keys_mean,
     pin_two_tokens_logistic, pin_torch_sdpa, pin_gqa_mapping, pin_scale_limits,
     pin_convex_hull, pin_every_live_token_matters, pin_poison_ignored,
     pin_shared_prefix_equals_private, pin_append_roundtrip, pin_copy_blocks, pin_bf16_decode,
+    pin_prefill_single_query_is_decode, pin_prefill_torch_sdpa_causal,
+    pin_prefill_chunk_rows_of_full, pin_prefill_future_keys_ignored,
 ]
 
 
@@ -453,11 +528,25 @@ def _layout_floor(tokens, block_size):
     return blocks, blocks * block_size - tokens
 
 
+def _positions_from_zero(seq_len, query_len):
+    return np.arange(query_len, dtype=np.int64)
+
+
+def _visible_exclusive(position, seq_len):
+    return position
+
+
+def _visible_all(position, seq_len):
+    return seq_len
+
+
 PLANTED = {
     "attend": [_attend_wrong_gqa, _attend_no_scale, _attend_no_max_shift, _attend_kv_swapped,
                _attend_drop_last],
     "translate": [_translate_swapped, _translate_off_by_one],
     "block_layout": [_layout_floor],
+    "chunk_positions": [_positions_from_zero],
+    "visible_prefix": [_visible_exclusive, _visible_all],
 }
 
 

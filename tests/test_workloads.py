@@ -112,3 +112,30 @@ def test_sweep_cells_small(b, d):
     assert (w.block_size, w.head_dim, w.num_heads, w.kv_heads) == (b, d, 32, 8)
     need = sum(oracle.block_layout(int(n), b)[0] for n in w.seq_lens)
     assert w.num_blocks == -(-5 * need // 4) + 1
+
+
+def test_prefill_workloads_shapes_and_determinism():
+    w = W.prefill_tiny()
+    assert w.num_queries == int(w.query_lens.sum())
+    assert list(w.query_start) == [0] + list(np.cumsum(w.query_lens))
+    assert np.all(w.query_lens <= w.seq_lens)
+    assert w.q.shape == (w.num_queries, w.num_heads, w.head_dim) and w.q.dtype == np.uint16
+    # every position of every sequence is cached; slots past the end hold NaN
+    for s, n in enumerate(w.seq_lens):
+        blocks, unused = oracle.block_layout(int(n), w.block_size)
+        if unused:
+            last = w.block_tables[s, blocks - 1]
+            assert np.all(w.k_cache[last, :, w.block_size - unused:, :] == W.BF16_NAN)
+    again = W.prefill_tiny()
+    assert np.array_equal(again.q, w.q) and np.array_equal(again.k_cache, w.k_cache)
+    big = W.prefill_llama70b(num_seqs=4)
+    assert np.array_equal(big.query_lens, big.seq_lens)
+    assert big.seq_lens.min() >= 500 and big.seq_lens.max() <= 700
+    ch = W.prefill_chunked(num_seqs=4)
+    assert np.all(ch.query_lens == 256) and np.all(ch.seq_lens >= 756)
+
+
+def test_prefill_flops_counts_causal_pairs():
+    lens, nq = [5, 9, 1], [5, 3, 1]
+    pairs = sum(p + 1 for n, c in zip(lens, nq) for p in range(n - c, n))
+    assert W.prefill_flops(lens, nq, num_heads=4, head_dim=8) == 4 * 8 * 4 * pairs

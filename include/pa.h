@@ -251,6 +251,44 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
                          int32_t num_pairs, int32_t num_blocks, int32_t kv_heads,
                          int32_t block_size, int32_t head_dim, int32_t dtype, void* stream);
 
+/*
+ * Chunked causal prefill over the paged cache: every sequence brings a chunk
+ * of queries whose K/V are already in the cache (pa_kv_append), at its last
+ * positions, and each query attends every position up to and including its
+ * own ("How PagedAttention works", section "A strong answer": the kernel
+ * gathers each query's blocks through the table; lihaoran.work explainer, section "A block
+ * table maps logical order to physical storage": full causal attention over
+ * the visible history).
+ *
+ *   out, q         [num_queries][num_heads][head_dim] bf16; sequence s owns
+ *                  rows [query_start[s], query_start[s+1])
+ *   k_cache,       [num_blocks][kv_heads][block_size][head_dim] bf16
+ *   v_cache
+ *   block_tables   int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens       int32 [num_seqs]: cached positions, chunk included; the
+ *                  chunk of n queries sits at positions seq_lens[s]-n .. -1
+ *   query_start    int32 [num_seqs + 1], non-decreasing, 0 .. num_queries
+ *   max_query_len  host upper bound on every chunk length (sizes the grid)
+ *
+ * All device pointers are caller-owned; the call is asynchronous on `stream`
+ * and allocates nothing.  Rows of a chunk that cannot be served (longer than
+ * its sequence or than max_query_len, or a sequence longer than its table)
+ * are NaN; a sequence whose offsets fall outside [0, num_queries] or decrease
+ * is skipped (its rows are not written); a table entry outside the pool
+ * makes the rows that read it NaN.  Host checks: negative sizes, a zero
+ * size, num_heads % kv_heads != 0, a non-finite scale, null or misaligned
+ * pointers -> PA_ERR_INVALID_ARG; fp32, head_dim not 64/128, block_size not a
+ * power of two in [16, 256], or a query group (num_heads / kv_heads) that is
+ * not a power of two <= 16 -> PA_ERR_UNSUPPORTED.  num_seqs, num_queries or
+ * max_query_len of 0 launch nothing.
+ */
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, const int32_t* query_start, int32_t max_query_len,
+                     int32_t num_seqs, int32_t num_queries, int32_t num_heads, int32_t kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                     int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -367,4 +367,52 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
                                          block_bytes, (hipStream_t)stream));
 }
 
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, const int32_t* query_start, int32_t max_query_len,
+                     int32_t num_seqs, int32_t num_queries, int32_t num_heads, int32_t kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                     int32_t dtype, void* stream) {
+  if (num_seqs < 0 || num_queries < 0 || max_query_len < 0 || num_heads <= 0 || kv_heads <= 0 ||
+      num_heads % kv_heads != 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || !dtype_ok(dtype) || !isfinite(scale))
+    return PA_ERR_INVALID_ARG;
+  const int32_t group = num_heads / kv_heads;
+  if (dtype != PA_BF16 || (head_dim != 64 && head_dim != 128) || !pow2(block_size) ||
+      block_size < 16 || block_size > 256 || !pow2(group) || group > 16)
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_queries == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_INVALID_ARG;
+  const int64_t q_tiles = ceil_div((int64_t)max_query_len * group, pa::kPrefillRows);
+  const int64_t pairs8 = round_up((int64_t)num_seqs * kv_heads, 8);
+  if (pairs8 * q_tiles > INT32_MAX) return PA_ERR_INVALID_ARG;
+
+  pa::PrefillParams p;
+  memset(&p, 0, sizeof(p));
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.query_start = query_start;
+  p.num_seqs = num_seqs;
+  p.num_queries = num_queries;
+  p.max_query_len = max_query_len;
+  p.num_heads = num_heads;
+  p.kv_heads = kv_heads;
+  p.group = group;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.block_shift = log2i(block_size);
+  p.q_tiles = (int32_t)q_tiles;
+  p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  return from_hip(pa::launch_prefill_mfma(p, head_dim, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -40,6 +40,29 @@ struct DecodeParams {
   float scale_log2;             // scale * log2(e): scores kept in base-2 units
 };
 
+// Everything a chunked-prefill launch needs.
+struct PrefillParams {
+  void* out;                    // [T][Hq][D] bf16
+  const void* q;                // [T][Hq][D] bf16: sequence s's chunk is rows query_start[s]..
+  const void* k_cache;          // [NB][Hkv][BS][D] bf16, the chunks already appended
+  const void* v_cache;
+  const int32_t* block_tables;  // [B][max_blocks_per_seq]
+  const int32_t* seq_lens;      // [B] cached positions, chunk included
+  const int32_t* query_start;   // [B+1] chunk offsets into q / out
+  int32_t num_seqs;
+  int32_t num_queries;          // T
+  int32_t max_query_len;        // host bound on any chunk
+  int32_t num_heads;
+  int32_t kv_heads;
+  int32_t group;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t block_shift;
+  int32_t q_tiles;              // query tiles per (sequence, KV head)
+  float scale_log2;
+};
+
 // Work-group index -> (kv head, sequence, partition).  Partition-major so that
 // every sequence's first partition is dispatched before any second one, and
 // consecutive work-groups (which the dispatcher spreads over the XCDs) walk
@@ -145,6 +168,10 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs
                               int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
 
 // is_bf16: element type of q/out/caches; head_dim in {64, 128}; group in {1,2,4,8}.
+// Rows of (position, query head) one prefill work-group covers.
+constexpr int kPrefillRows = 256;
+hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t stream);
+
 hipError_t launch_decode_valu(const DecodeParams& p, bool is_bf16, int head_dim,
                               hipStream_t stream);
 

@@ -1,0 +1,270 @@
+// Chunked paged prefill on the gfx950 matrix cores (bf16 storage, fp32
+// accumulation).
+//
+// Each sequence brings a chunk of queries whose keys and values are already
+// in the cache: the last n of its L cached positions (a whole prompt when
+// n = L).  The query at position p attends positions [0, p] through the
+// sequence's block table (lihaoran.work PagedAttention explainer, section "A
+// block table maps logical order to physical storage": causal attention over
+// the visible history; logical block t / block_size, slot t % block_size).
+//
+// Rows are (chunk query, query head) pairs of one KV head's GQA group: row r
+// of a work-group is query i0 + r / G, head g = r % G, so the G heads that
+// share a KV head share every K/V load.  A work-group of 4 waves covers
+// kPrefillRows rows; each wave owns 64 of them as four 16-row column tiles
+// of the MFMA step from mfma_step.h (S^T = K Q^T, O^T += V^T P^T; its Q rows
+// wait in LDS, read back as the B operands of every step), and walks
+// the keys [0, last position of its rows] in 32-token steps, loading each
+// step once for its four tiles and one step ahead of the math.  The causal
+// limit is per lane (a lane's score column is one row); V rows past the
+// wave's last key are zeroed so tail slots never reach the sum.  The first
+// step holds key 0, which every row sees, so no row's running max stays
+// -inf after it.
+//
+// Work order: work-group x runs on XCD x % 8.  All query tiles of one
+// (sequence, KV head) pair are given consecutive slots on one XCD, latest
+// tile (most keys) first, so the pair's K/V stays in that XCD's L2 while its
+// tiles run.
+#include "mfma_step.h"
+
+namespace pa {
+namespace {
+
+using namespace mfma;
+
+constexpr int kPfWaves = 4;
+constexpr int kRowTiles = 4;                 // 16-row MFMA column tiles per wave
+constexpr int kWaveRows = 16 * kRowTiles;
+static_assert(kPfWaves * kWaveRows == kPrefillRows, "work-group rows");
+// LDS bytes per staged Q row: 16 bytes of padding move consecutive rows to
+// other banks, so the 16 lanes that read one 16-byte column of 16 rows do
+// not collide.
+template <int D>
+constexpr int kQStride = D * 2 + 16;
+
+// One 32-key step for all row tiles of a wave.  Keys > lim[nr] (the lane's
+// row position) are masked; V rows at or past kend are zeroed.
+// Q^T operands come from the wave's rows staged in LDS (qlds: this lane's
+// row of tile 0, kQStride bytes per row).
+template <int D>
+__device__ inline void prefill_step(StepRegs<D>& r, Acc<D> (&a)[kRowTiles],
+                                    const unsigned char* qlds, int base, int kend,
+                                    const int (&lim)[kRowTiles], float scale_log2, int q4) {
+  constexpr int kKi = D / 32;
+  constexpr int kVd = D / 16;
+  if (base + 32 > kend) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = base + 16 * (e >> 2) + 4 * q4 + (e & 3);
+      if (tok >= kend) r.v[e] = typename VRow<D>::T{};
+    }
+  }
+  // V^T operands of the step (token order tau(q4, e)), shared by the tiles
+  u32x4 av[kVd];
+#pragma unroll
+  for (int jt = 0; jt < kVd; ++jt) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t lo = r.v[2 * u][jt >> 1];
+      const uint32_t hi = r.v[2 * u + 1][jt >> 1];
+      av[jt][u] = (jt & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
+                           : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+  }
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+    f32x4 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kKi; ++i)
+        s[kt] = mma(r.k[kt][i], *(const u32x4*)(qlds + nr * 16 * kQStride<D> + 64 * i), s[kt]);
+    }
+    float t[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tok = base + 16 * (e >> 2) + 4 * q4 + (e & 3);
+      const float v = s[e >> 2][e & 3] * scale_log2;
+      t[e] = tok <= lim[nr] ? v : -INFINITY;
+      mx = fmaxf(mx, t[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(a[nr].m, mx);
+    const float keep = exp2f(a[nr].m - m_new);  // 0 on the first step
+    u32x4 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t lo = f32_to_bf16(exp2f(t[2 * u] - m_new));
+      const uint32_t hi = f32_to_bf16(exp2f(t[2 * u + 1] - m_new));
+      pb[u] = lo | (hi << 16);
+      psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
+    }
+    a[nr].l = a[nr].l * keep + psum;
+    a[nr].m = m_new;
+#pragma unroll
+    for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt] * keep);
+  }
+}
+
+// A lane's part of one output row: head-dimension values [d0, d0 + D/16).
+template <int D>
+__device__ inline void store_row_part(uint16_t* dst, const float* v) {
+  constexpr int kVd = D / 16;
+  uint32_t w[kVd / 2];
+#pragma unroll
+  for (int j = 0; j < kVd / 2; ++j)
+    w[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
+  if constexpr (kVd == 8)
+    *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+  else
+    *(u32x2*)dst = u32x2{w[0], w[1]};
+}
+
+template <int D>
+__global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillParams p) {
+  constexpr int kVd = D / 16;
+  const int pairs = p.num_seqs * p.kv_heads;
+  const int x = blockIdx.x;
+  const int slot = x >> 3;
+  const int pair = (slot / p.q_tiles) * 8 + (x & 7);
+  if (pair >= pairs) return;
+  const int tile = p.q_tiles - 1 - (slot % p.q_tiles);
+  const int seq = pair / p.kv_heads;
+  const int head = pair - seq * p.kv_heads;
+  const int q0 = p.query_start[seq];
+  const int q1 = p.query_start[seq + 1];
+  if (q0 < 0 || q1 > p.num_queries || q1 <= q0) return;  // no chunk, or offsets out of range
+  const int nq = q1 - q0;
+  const int len = p.seq_lens[seq];
+  const int G = p.group;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int q4 = lane >> 4;
+  uint16_t* out = (uint16_t*)p.out;
+  const int64_t row_stride = (int64_t)p.num_heads * D;  // elements per query
+  const int64_t head0 = (int64_t)head * G * D;
+
+  // A chunk the launch cannot serve (longer than its sequence or than the
+  // host's bound, or a sequence past the table) gets NaN in every row of
+  // this head group, written by tile 0; no cache or table read happens.
+  const bool servable = nq <= len && nq <= p.max_query_len &&
+                        (int64_t)len <= (int64_t)p.max_blocks_per_seq * p.block_size;
+  if (!servable) {
+    if (tile != 0) return;
+    for (int64_t i = tid; i < (int64_t)nq * G * D; i += kPfWaves * 64) {
+      const int64_t qi = i / (G * D);
+      out[(q0 + qi) * row_stride + head0 + (i - qi * G * D)] = 0x7FC0;
+    }
+    return;
+  }
+  const int i0 = tile * (kPrefillRows / G);  // first chunk query of the work-group
+  const int wrow0 = wave * kWaveRows;
+  const int wi_first = i0 + wrow0 / G;
+  if (wi_first >= nq) return;  // this wave has no rows (the kernel has no barrier)
+  const int wi_last = min(nq - 1, i0 + (wrow0 + kWaveRows - 1) / G);
+  const int pos0 = len - nq;   // position of chunk query 0
+  const int kend = pos0 + wi_last + 1;
+
+  // The wave stages its 64 Q rows in LDS (zero rows past the chunk); each
+  // lane keeps the causal limit of its row in every tile.
+  __shared__ __attribute__((aligned(16))) unsigned char sm_q[kPfWaves][kWaveRows * kQStride<D>];
+  unsigned char* wq = sm_q[wave];
+  {
+    constexpr int kParts = D * 2 / 16;  // 16-byte parts per row
+    for (int k = lane; k < kWaveRows * kParts; k += 64) {
+      const int rw = k / kParts;
+      const int part = k - rw * kParts;
+      const int row = wrow0 + rw;
+      const int qi = i0 + row / G;
+      const int g = row - (row / G) * G;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (qi < nq)
+        v = *(const u32x4*)((const char*)p.q +
+                            ((int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D) * 2 + part * 16);
+      *(u32x4*)(wq + rw * kQStride<D> + part * 16) = v;
+    }
+  }
+  int lim[kRowTiles];
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+    const int qi = i0 + (wrow0 + 16 * nr + r16) / G;
+    lim[nr] = qi < nq ? pos0 + qi : 0;
+  }
+  __builtin_amdgcn_wave_barrier();  // one wave's LDS writes and reads stay in order
+  const unsigned char* qlds = wq + r16 * kQStride<D> + q4 * 16;
+
+  SeqView c;
+  const int64_t head_stride = (int64_t)p.block_size * D * 2;
+  c.kbase = (const char*)p.k_cache + (int64_t)head * head_stride;
+  c.vbase = (const char*)p.v_cache + (int64_t)head * head_stride;
+  c.table = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
+  c.block_stride = (int64_t)p.kv_heads * head_stride;
+  c.nblocks_valid = (len + p.block_size - 1) >> p.block_shift;
+  c.num_blocks = p.num_blocks;
+  c.block_shift = p.block_shift;
+  c.bmask = p.block_size - 1;
+
+  Acc<D> a[kRowTiles];
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) reset(a[nr]);
+  bool bad = false;
+
+  int base = 0;
+  {
+    StepRegs<D> ra, rb;
+    load_step<D, false>(ra, c, base, r16, q4, bad);
+    while (true) {
+      int next = base + 32;
+      if (next < kend) load_step<D, false>(rb, c, next, r16, q4, bad);
+      prefill_step<D>(ra, a, qlds, base, kend, lim, p.scale_log2, q4);
+      base = next;
+      if (base >= kend) break;
+      next = base + 32;
+      if (next < kend) load_step<D, false>(ra, c, next, r16, q4, bad);
+      prefill_step<D>(rb, a, qlds, base, kend, lim, p.scale_log2, q4);
+      base = next;
+      if (base >= kend) break;
+    }
+  }
+
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+    finish_wave(a[nr], bad);
+    const int row = wrow0 + 16 * nr + r16;
+    const int qi = i0 + row / G;
+    const int g = row - (row / G) * G;
+    if (qi >= nq) continue;
+    const float inv = 1.0f / a[nr].l;
+    uint16_t* orow = out + (int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float v[kVd];
+#pragma unroll
+      for (int jt = 0; jt < kVd; ++jt) v[jt] = a[nr].o[jt][rr] * inv;
+      store_row_part<D>(orow + kVd * (4 * q4 + rr), v);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t stream) {
+  const int64_t pairs8 = ((int64_t)p.num_seqs * p.kv_heads + 7) / 8 * 8;
+  const dim3 grid((unsigned)(pairs8 * p.q_tiles));
+  const dim3 block(kPfWaves * 64);
+  if (head_dim == 128)
+    prefill_mfma_kernel<128><<<grid, block, 0, stream>>>(p);
+  else if (head_dim == 64)
+    prefill_mfma_kernel<64><<<grid, block, 0, stream>>>(p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pa

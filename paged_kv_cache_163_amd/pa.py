@@ -14,6 +14,8 @@ Tensor layouts (C-contiguous):
     k_new, v_new        [num_tokens, kv_heads, head_dim]
     slot_mapping        int64 [num_tokens]
     block_mapping       int64 [num_pairs, 2]   (src, dst)
+    prefill q, out      [num_queries, num_heads, head_dim]       bfloat16
+    query_start         int32 [num_seqs + 1]   chunk offsets into the prefill q
 """
 
 from __future__ import annotations
@@ -64,10 +66,12 @@ _decode_append = _sig("pa_decode_append", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _v
                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32,
                       _vp)
 _copy_blocks = _sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
+_prefill = _sig("pa_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                _i32, _i32, _i32, _i32, _f32, _i32, _vp)
 
 EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_append",
             "pa_decode_plan", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_ex",
-            "pa_decode_append", "pa_copy_blocks"]
+            "pa_decode_append", "pa_copy_blocks", "pa_prefill"]
 
 
 def abi_version() -> int:
@@ -245,4 +249,41 @@ def decode_append(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_tables,
                         _dev(slot_mapping, "slot_mapping", torch.int64), *common, float(scale),
                         int(partition_size), ws_ptr, ws_len, dt, KERNELS[kernel], _stream(stream))
     _check(st, "decode_append")
+    return out
+
+
+def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale, max_query_len=None,
+            out=None, stream=None):
+    """Chunked causal prefill over the paged cache (bf16).
+
+    Sequence s's chunk is rows query_start[s]..query_start[s+1] of ``q``; its
+    queries are the last positions of the seq_lens[s] cached ones (their K/V
+    already appended) and each attends every position up to its own.
+    ``max_query_len`` bounds every chunk (read from ``query_start`` when not
+    given, which synchronises with the device).
+    """
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k_cache and v_cache must share a dtype")
+    T, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shape does not match q")
+    B = seq_lens.shape[0] if seq_lens.dim() == 1 else -1
+    if B < 0 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq], seq_lens [num_seqs]")
+    if query_start.dim() != 1 or query_start.shape[0] != B + 1:
+        raise ValueError("query_start must be [num_seqs + 1]")
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if B > 0 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    st = _prefill(_dev(out, "out", ndim=3), _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
+                  _dev(v_cache, "v_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32),
+                  block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
+                  _dev(query_start, "query_start", torch.int32), int(max_query_len), B, T, hq, hkv,
+                  d, bs, nb, float(scale), dt, _stream(stream))
+    _check(st, "prefill")
     return out

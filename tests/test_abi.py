@@ -157,3 +157,40 @@ def test_host_validation_rejects_before_launch(built_lib):
     assert cp(fake, fake, fake, i32(-2), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID
     assert cp(fake, fake, fake, i32(0), i32(8), i32(2), i32(16), i32(64), i32(1), None) == 0
     assert cp(fake, fake, None, i32(2), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID
+
+
+def test_prefill_host_validation(built_lib):
+    lib = ctypes.CDLL(built_lib)
+    vp = ctypes.c_void_p
+    fake = vp(4096)  # never dereferenced: every call below returns before a launch
+    pf = lib.pa_prefill
+    pf.restype = ctypes.c_int32
+    args = dict(out=fake, q=fake, k=fake, v=fake, bt=fake, maxblk=4, sl=fake, qs=fake, maxq=16,
+                B=2, T=20, hq=8, hkv=2, d=64, bs=16, nb=8, scale=0.125, dt=1, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        i = ctypes.c_int32
+        return pf(a["out"], a["q"], a["k"], a["v"], a["bt"], i(a["maxblk"]), a["sl"], a["qs"],
+                  i(a["maxq"]), i(a["B"]), i(a["T"]), i(a["hq"]), i(a["hkv"]), i(a["d"]),
+                  i(a["bs"]), i(a["nb"]), ctypes.c_float(a["scale"]), i(a["dt"]), a["stream"])
+
+    INVALID, UNSUPPORTED = 1, 2
+    assert call(hq=9) == INVALID
+    assert call(B=-1) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(maxq=-1) == INVALID
+    assert call(nb=0) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(dt=5) == INVALID
+    assert call(qs=None) == INVALID
+    assert call(q=vp(4100)) == INVALID                # not 16-byte aligned
+    assert call(dt=0) == UNSUPPORTED                  # fp32: no prefill kernel
+    assert call(d=96) == UNSUPPORTED
+    assert call(bs=8) == UNSUPPORTED                  # block below a 16-token tile
+    assert call(hq=6, hkv=2) == UNSUPPORTED           # group of 3
+    assert call(hq=64, hkv=2) == UNSUPPORTED          # group of 32
+    # a grid beyond 2^31 work-groups
+    assert call(B=1 << 20, hkv=2, maxq=1 << 20, T=1 << 20) == INVALID
+    for empty in (dict(B=0), dict(T=0), dict(maxq=0)):
+        assert call(**empty) == 0                     # nothing to do, nothing launched

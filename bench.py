@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama70b",
-                    help="llama70b | shared_prefix | long_context | sweep_b{16,32,64}_d{64,128}")
+                    help="llama70b | shared_prefix | long_context | sweep_b{16,32,64}_d{64,128} "
+                         "| prefill_llama70b | prefill_chunked (one pa_prefill launch per step)")
     ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled over steps")
     ap.add_argument("--partition", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "valu"])
@@ -161,6 +162,121 @@ def cpu_baseline(w, seconds: float):
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, vendor figure
+PREFILL_METRIC = "paged chunked prefill attention: achieved TFLOP/s (% of bf16 MFMA peak), 1 GPU"
+
+
+def prefill_cpu_baseline(w, seconds: float):
+    """The oracle, as it stands, on query rows of the batch until ~seconds pass."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_163_amd import workloads as W
+    order = np.random.default_rng(123).permutation(w.num_queries)
+    starts = w.query_start
+    done, flops = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and done < w.num_queries:
+        r = int(order[done])
+        oracle.paged_prefill(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.query_lens,
+                             w.scale, w.block_size, rows=[r])
+        s = int(np.searchsorted(starts, r, side="right")) - 1
+        pos = int(w.seq_lens[s] - w.query_lens[s] + (r - starts[s]))
+        flops += W.prefill_flops([pos + 1], [1], w.num_heads, w.head_dim)
+        done += 1
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(flops / dt / 1e12, 9),
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} query rows of the {w.name} batch (random order, seed 123, each "
+                   f"with its sequence's gather), {dt:.1f} s single process, numpy float64; "
+                   f"host has {os.cpu_count()} logical CPUs"),
+    }
+
+
+def prefill_main(args, np, torch, W, pa, dev):
+    """One step = one pa_prefill launch over the whole batch of chunks."""
+    w = W.PREFILL_WORKLOADS[args.workload]()
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    pools = [(to_dev(w.k_cache), to_dev(w.v_cache)) for _ in range(max(1, args.rotate))]
+    q, bt, lens, qs = to_dev(w.q), to_dev(w.block_tables), to_dev(w.seq_lens), to_dev(w.query_start)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kc, vc = pools[i % len(pools)]
+        pa.prefill(q, kc, vc, bt, lens, qs, w.scale, max_query_len=w.max_query_len, out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer = HipTimer()
+    t_start, t_end = timer.event(), timer.event()
+    timer.record(t_start, stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    timer.record(t_end, stream)
+    torch.cuda.synchronize()
+    step_ms = timer.elapsed_ms(t_start, t_end) / args.steps
+    timer.close()
+    flops = W.prefill_flops(w.seq_lens, w.query_lens, w.num_heads, w.head_dim)
+    tflops = flops / (step_ms * 1e-3) / 1e12
+    kv_bytes = W.decode_kv_bytes(w.seq_lens, w.kv_heads, w.head_dim, w.elem_bytes)
+    line = {
+        "metric": PREFILL_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs,
+            "num_queries": w.num_queries,
+            "num_heads": w.num_heads,
+            "kv_heads": w.kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "mean_seq_len": round(float(w.seq_lens.mean()), 2),
+            "mean_chunk": round(float(w.query_lens.mean()), 2),
+            "pool_rotation": len(pools),
+            "parallelism": "single GPU",
+        },
+        "flops_per_step": flops,
+        "tokens_per_s": round(w.num_queries / (step_ms * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "prefill_mfma_kernel",
+            "flops_per_launch": flops,
+            "avg_launch_ms": round(step_ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -180,6 +296,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.workload in W.PREFILL_WORKLOADS:
+        return prefill_main(args, np, torch, W, pa, dev)
 
     if args.copy_calibration:
         n = 1 << 30

@@ -33,7 +33,7 @@ namespace {
 using namespace mfma;
 
 constexpr int kPfWaves = 4;
-constexpr int kRowTiles = 4;                 // 16-row MFMA column tiles per wave
+constexpr int kRowTiles = 3;                 // 16-row MFMA column tiles per wave
 constexpr int kWaveRows = 16 * kRowTiles;
 static_assert(kPfWaves * kWaveRows == kPrefillRows, "work-group rows");
 // LDS bytes per staged Q row: 16 bytes of padding move consecutive rows to
@@ -42,14 +42,47 @@ static_assert(kPfWaves * kWaveRows == kPrefillRows, "work-group rows");
 template <int D>
 constexpr int kQStride = D * 2 + 16;
 
-// One 32-key step for all row tiles of a wave.  Keys > lim[nr] (the lane's
-// row position) are masked; V rows at or past kend are zeroed.
-// Q^T operands come from the wave's rows staged in LDS (qlds: this lane's
-// row of tile 0, kQStride bytes per row).
+// A row's running state: O^T tiles, the row sum (computed on the matrix core
+// as P^T against a ones operand, so it is the exact sum of the bf16 P the
+// output uses; all four elements hold the lane's row sum) and the reference
+// max the probabilities are taken against (base-2 units).
 template <int D>
-__device__ inline void prefill_step(StepRegs<D>& r, Acc<D> (&a)[kRowTiles],
+struct PfAcc {
+  f32x4 o[D / 16];
+  f32x4 l;
+  float m;
+};
+
+// How far (base-2 units) a row's step max may rise above its reference max
+// before O and l are rescaled: probabilities stay <= 2^8, harmless in fp32 and
+// bf16, and most steps skip the rescale of the accumulators.
+constexpr float kSlack = 8.0f;
+
+// Max over the four lanes that share r16 (one per 16-lane row of the wave).
+__device__ inline float row_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {  // round to nearest even
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// One 32-key step for all row tiles of a wave.  With kMask, keys > lim[nr]
+// (the lane's row position) are masked; V rows at or past kend are zeroed.
+// Q^T operands come from the wave's rows staged in LDS (qlds: this lane's
+// row of tile 0, kQStride bytes per row).  c = scale * log2(e) > 0.
+template <int D, bool kMask>
+__device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
                                     const unsigned char* qlds, int base, int kend,
-                                    const int (&lim)[kRowTiles], float scale_log2, int q4) {
+                                    const int (&lim)[kRowTiles], float c, int q4) {
   constexpr int kKi = D / 32;
   constexpr int kVd = D / 16;
   if (base + 32 > kend) {
@@ -71,6 +104,7 @@ __device__ inline void prefill_step(StepRegs<D>& r, Acc<D> (&a)[kRowTiles],
                            : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
   }
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr) {
     f32x4 s[2];
@@ -81,32 +115,35 @@ __device__ inline void prefill_step(StepRegs<D>& r, Acc<D> (&a)[kRowTiles],
       for (int i = 0; i < kKi; ++i)
         s[kt] = mma(r.k[kt][i], *(const u32x4*)(qlds + nr * 16 * kQStride<D> + 64 * i), s[kt]);
     }
-    float t[8];
-    float mx = -INFINITY;
+    float sv[8];
+    float mr = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int tok = base + 16 * (e >> 2) + 4 * q4 + (e & 3);
-      const float v = s[e >> 2][e & 3] * scale_log2;
-      t[e] = tok <= lim[nr] ? v : -INFINITY;
-      mx = fmaxf(mx, t[e]);
+      sv[e] = s[e >> 2][e & 3];
+      if constexpr (kMask) {
+        const int tok = base + 16 * (e >> 2) + 4 * q4 + (e & 3);
+        sv[e] = tok <= lim[nr] ? sv[e] : -INFINITY;
+      }
+      mr = fmaxf(mr, sv[e]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(a[nr].m, mx);
-    const float keep = exp2f(a[nr].m - m_new);  // 0 on the first step
+    const float mx = row_max4(mr) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > a[nr].m + kSlack) != 0) {  // wave-uniform
+      const float m_new = fmaxf(a[nr].m, mx);
+      const float keep = __builtin_amdgcn_exp2f(a[nr].m - m_new);  // 0 on the first step
+#pragma unroll
+      for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] *= keep;
+      a[nr].l *= keep;
+      a[nr].m = m_new;
+    }
+    const float nm = -a[nr].m;
     u32x4 pb;
-    float psum = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t lo = f32_to_bf16(exp2f(t[2 * u] - m_new));
-      const uint32_t hi = f32_to_bf16(exp2f(t[2 * u + 1] - m_new));
-      pb[u] = lo | (hi << 16);
-      psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
-    }
-    a[nr].l = a[nr].l * keep + psum;
-    a[nr].m = m_new;
+    for (int u = 0; u < 4; ++u)
+      pb[u] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sv[2 * u], c, nm)),
+                        __builtin_amdgcn_exp2f(fmaf(sv[2 * u + 1], c, nm)));
+    a[nr].l = mma(ones, pb, a[nr].l);
 #pragma unroll
-    for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt] * keep);
+    for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt]);
   }
 }
 
@@ -210,9 +247,14 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillPara
   c.block_shift = p.block_shift;
   c.bmask = p.block_size - 1;
 
-  Acc<D> a[kRowTiles];
+  PfAcc<D> a[kRowTiles];
 #pragma unroll
-  for (int nr = 0; nr < kRowTiles; ++nr) reset(a[nr]);
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+#pragma unroll
+    for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    a[nr].l = f32x4{0.f, 0.f, 0.f, 0.f};
+    a[nr].m = -INFINITY;
+  }
   bool bad = false;
 
   int base = 0;
@@ -222,12 +264,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillPara
     while (true) {
       int next = base + 32;
       if (next < kend) load_step<D, false>(rb, c, next, r16, q4, bad);
-      prefill_step<D>(ra, a, qlds, base, kend, lim, p.scale_log2, q4);
+      prefill_step<D, true>(ra, a, qlds, base, kend, lim, p.scale_log2, q4);
       base = next;
       if (base >= kend) break;
       next = base + 32;
       if (next < kend) load_step<D, false>(ra, c, next, r16, q4, bad);
-      prefill_step<D>(rb, a, qlds, base, kend, lim, p.scale_log2, q4);
+      prefill_step<D, true>(rb, a, qlds, base, kend, lim, p.scale_log2, q4);
       base = next;
       if (base >= kend) break;
     }
@@ -235,12 +277,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillPara
 
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr) {
-    finish_wave(a[nr], bad);
     const int row = wrow0 + 16 * nr + r16;
     const int qi = i0 + row / G;
     const int g = row - (row / G) * G;
     if (qi >= nq) continue;
-    const float inv = 1.0f / a[nr].l;
+    const float inv = bad ? __builtin_nanf("") : 1.0f / a[nr].l[0];
     uint16_t* orow = out + (int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {

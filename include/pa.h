@@ -276,7 +276,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
  * are NaN; a sequence whose offsets fall outside [0, num_queries] or decrease
  * is skipped (its rows are not written); a table entry outside the pool
  * makes the rows that read it NaN.  Host checks: negative sizes, a zero
- * size, num_heads % kv_heads != 0, a non-finite scale, null or misaligned
+ * size, num_heads % kv_heads != 0, a scale that is not finite and positive
+ * (the kernel takes row maxima of unscaled scores), null or misaligned
  * pointers -> PA_ERR_INVALID_ARG; fp32, head_dim not 64/128, block_size not a
  * power of two in [16, 256], or a query group (num_heads / kv_heads) that is
  * not a power of two <= 16 -> PA_ERR_UNSUPPORTED.  num_seqs, num_queries or

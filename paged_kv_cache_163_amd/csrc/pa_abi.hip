@@ -375,7 +375,7 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
                      int32_t dtype, void* stream) {
   if (num_seqs < 0 || num_queries < 0 || max_query_len < 0 || num_heads <= 0 || kv_heads <= 0 ||
       num_heads % kv_heads != 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
-      max_blocks_per_seq <= 0 || !dtype_ok(dtype) || !isfinite(scale))
+      max_blocks_per_seq <= 0 || !dtype_ok(dtype) || !isfinite(scale) || !(scale > 0.0f))
     return PA_ERR_INVALID_ARG;
   const int32_t group = num_heads / kv_heads;
   if (dtype != PA_BF16 || (head_dim != 64 && head_dim != 128) || !pow2(block_size) ||

@@ -78,7 +78,8 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {  // round to nearest 
 // One 32-key step for all row tiles of a wave.  With kMask, keys > lim[nr]
 // (the lane's row position) are masked; V rows at or past kend are zeroed.
 // Q^T operands come from the wave's rows staged in LDS (qlds: this lane's
-// row of tile 0, kQStride bytes per row).  c = scale * log2(e) > 0.
+// row of tile 0, kQStride bytes per row).  c = scale * log2(e) > 0 (the host
+// rejects other scales), so the row max of c*s is c times the max of s.
 template <int D, bool kMask>
 __device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
                                     const unsigned char* qlds, int base, int kend,

@@ -182,6 +182,8 @@ def test_prefill_host_validation(built_lib):
     assert call(maxq=-1) == INVALID
     assert call(nb=0) == INVALID
     assert call(scale=float("inf")) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(scale=-0.125) == INVALID
     assert call(dt=5) == INVALID
     assert call(qs=None) == INVALID
     assert call(q=vp(4100)) == INVALID                # not 16-byte aligned

@@ -36,6 +36,7 @@ from .paged_attention import (  # noqa: F401
     kv_append,
     paged_decode,
     paged_prefill,
+    swap_blocks,
     to_f64,
     translate,
     visible_prefix,

@@ -282,3 +282,18 @@ def copy_blocks(k_cache, v_cache, pairs) -> None:
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
         k_cache[dst] = k_cache[src]
         v_cache[dst] = v_cache[src]
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs) -> None:
+    """Move whole blocks from one pool into another, in place.
+
+    "How PagedAttention works", feature table row on preemption and section
+    "What interviewers probe next": a preempted sequence's blocks go to pinned
+    host memory (and come back) a block at a time.  Each (src, dst) pair
+    copies every KV head and every slot of block src of the source pool,
+    keys and values, into block dst of the destination pool; the two pools
+    share the block shape and may differ in size.  Raw bits, so exact.
+    """
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]

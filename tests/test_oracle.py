@@ -409,6 +409,35 @@ def pin_prefill_future_keys_ignored():
     return True
 
 
+def pin_swap_round_trip():
+    """Blocks swapped out to a second (host) pool and back into other blocks
+    come back bit-identical; every block not named stays as it was; within one
+    pool a swap is the copy-on-write block copy."""
+    rng = np.random.default_rng(31)
+    dev_k = rng.standard_normal((12, 2, 4, 8)).astype(np.float32)
+    dev_v = rng.standard_normal((12, 2, 4, 8)).astype(np.float32)
+    host_k = np.full((5, 2, 4, 8), np.nan, dtype=np.float32)
+    host_v = host_k.copy()
+    out_pairs = [(3, 0), (7, 4), (11, 2)]
+    oracle.swap_blocks(host_k, host_v, dev_k, dev_v, out_pairs)
+    if not (np.array_equal(host_k[[0, 4, 2]], dev_k[[3, 7, 11]])
+            and np.array_equal(host_v[[0, 4, 2]], dev_v[[3, 7, 11]])
+            and np.all(np.isnan(host_k[[1, 3]])) and np.all(np.isnan(host_v[[1, 3]]))):
+        return False
+    back_k, back_v = dev_k.copy(), dev_v.copy()
+    oracle.swap_blocks(back_k, back_v, host_k, host_v, [(0, 5), (4, 6), (2, 8)])
+    others = [b for b in range(12) if b not in (5, 6, 8)]
+    if not (np.array_equal(back_k[[5, 6, 8]], dev_k[[3, 7, 11]])
+            and np.array_equal(back_v[[5, 6, 8]], dev_v[[3, 7, 11]])
+            and np.array_equal(back_k[others], dev_k[others])
+            and np.array_equal(back_v[others], dev_v[others])):
+        return False
+    a_k, a_v, b_k, b_v = dev_k.copy(), dev_v.copy(), dev_k.copy(), dev_v.copy()
+    oracle.swap_blocks(a_k, a_v, a_k, a_v, [(1, 9), (2, 10)])
+    oracle.copy_blocks(b_k, b_v, [(1, 9), (2, 10)])
+    return np.array_equal(a_k, b_k) and np.array_equal(a_v, b_v)
+
+
 ALL_PINS = [
     pin_block_layout_golden, pin_block_layout_bounds, pin_translation_golden,
     pin_paged_equals_contiguous, pin_single_token, pin_equal_keys_mean,
@@ -416,7 +445,7 @@ ALL_PINS = [
     pin_convex_hull, pin_every_live_token_matters, pin_poison_ignored,
     pin_shared_prefix_equals_private, pin_append_roundtrip, pin_copy_blocks, pin_bf16_decode,
     pin_prefill_single_query_is_decode, pin_prefill_torch_sdpa_causal,
-    pin_prefill_chunk_rows_of_full, pin_prefill_future_keys_ignored,
+    pin_prefill_chunk_rows_of_full, pin_prefill_future_keys_ignored, pin_swap_round_trip,
 ]
 
 
@@ -540,6 +569,17 @@ def _visible_all(position, seq_len):
     return seq_len
 
 
+def _swap_reversed(dst_k, dst_v, src_k, src_v, pairs):
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        dst_k[src] = src_k[dst]
+        dst_v[src] = src_v[dst]
+
+
+def _swap_keys_only(dst_k, dst_v, src_k, src_v, pairs):
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        dst_k[dst] = src_k[src]
+
+
 PLANTED = {
     "attend": [_attend_wrong_gqa, _attend_no_scale, _attend_no_max_shift, _attend_kv_swapped,
                _attend_drop_last],
@@ -547,6 +587,7 @@ PLANTED = {
     "block_layout": [_layout_floor],
     "chunk_positions": [_positions_from_zero],
     "visible_prefix": [_visible_exclusive, _visible_all],
+    "swap_blocks": [_swap_reversed, _swap_keys_only],
 }
 
 

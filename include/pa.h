@@ -290,6 +290,36 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                      int32_t dtype, void* stream);
 
+/*
+ * Block swap for preemption: move whole blocks between the device pool and a
+ * pinned host pool, either way ("How PagedAttention works", section "A strong
+ * answer", feature table: preemption swaps blocks to host memory at block
+ * granularity; section "What interviewers probe next": over the host link
+ * into pinned host memory).  For each (src, dst) pair of block_mapping,
+ * block src of the source pool (K and V, every KV head and slot) is copied
+ * bit-exactly into block dst of the destination pool.
+ *
+ *   dst_k, dst_v     destination pool, [dst_num_blocks][kv_heads][block_size][head_dim]
+ *   src_k, src_v     source pool, [src_num_blocks][...] with the same block shape
+ *   block_mapping    int64 [num_pairs][2] (src, dst), device or pinned host memory
+ *
+ * Each pool is either device memory or pinned host memory (hipHostMalloc,
+ * torch pin_memory); the GPU reaches host memory through its mapping, so the
+ * copy is one kernel whatever the pair count.  Device-to-device works too (a
+ * move between two device pools).  Host checks, before any launch: every
+ * pointer's residency is queried (hipPointerGetAttributes), and pageable or
+ * unknown memory, K and V of one pool in different places, misalignment
+ * (16 bytes, 8 for the mapping), negative or zero sizes -> PA_ERR_INVALID_ARG;
+ * host-to-host, or a block size not a multiple of 16 bytes ->
+ * PA_ERR_UNSUPPORTED.  Pairs naming a block outside either pool are skipped.
+ * Destination blocks must be distinct and must not be a source of the same
+ * call.  Asynchronous on `stream`; num_pairs = 0 launches nothing.
+ */
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const void* src_k,
+                         const void* src_v, int64_t src_num_blocks, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t kv_heads, int32_t block_size,
+                         int32_t head_dim, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,12 +40,17 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(
   *dst = *src;
 }
 
-// Copy-on-write ("How PagedAttention works", feature table: a fork copies only
-// the block that diverges).  Work-group index -> (pair, K or V, chunk of the
-// block); the chunk loop strides by the grid's chunk count.
-__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
-    u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, const int64_t* __restrict__ pairs,
-    int64_t num_blocks, int64_t block_vecs, int chunks) {
+// Whole-block moves between two pools with the same block shape: the
+// copy-on-write copy inside one pool ("How PagedAttention works", feature
+// table: a fork copies only the block that diverges) and the preemption swap
+// between the device pool and a pinned host pool (same table: swap blocks to
+// host memory at block granularity).  Work-group index -> (pair, K or V,
+// chunk of the block); the chunk loop strides by the grid's chunk count.
+// Pairs naming a block outside either pool are skipped.  Host memory is
+// reached through its device mapping, 16 bytes per lane.
+__global__ __launch_bounds__(kThreads) void move_blocks_kernel(
+    u32x4* dst_k, u32x4* dst_v, int64_t dst_blocks, const u32x4* src_k, const u32x4* src_v,
+    int64_t src_blocks, const int64_t* __restrict__ pairs, int64_t block_vecs, int chunks) {
   const int wg = blockIdx.x;
   const int chunk = wg % chunks;
   const int rest = wg / chunks;
@@ -53,10 +58,9 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   const int pair = rest >> 1;
   const int64_t src = pairs[2 * pair];
   const int64_t dst = pairs[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  u32x4* cache = is_v ? v_cache : k_cache;
-  const u32x4* from = cache + src * block_vecs;
-  u32x4* to = cache + dst * block_vecs;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const u32x4* from = (is_v ? src_v : src_k) + src * block_vecs;
+  u32x4* to = (is_v ? dst_v : dst_k) + dst * block_vecs;
   for (int64_t i = (int64_t)chunk * kThreads + threadIdx.x; i < block_vecs;
        i += (int64_t)chunks * kThreads)
     to[i] = from[i];
@@ -76,14 +80,16 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
-                              int64_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+hipError_t launch_move_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, const void* src_k,
+                              const void* src_v, int64_t src_blocks, const int64_t* pairs,
+                              int num_pairs, int64_t block_bytes, hipStream_t stream) {
   const int64_t block_vecs = block_bytes / 16;
   int64_t chunks = (block_vecs + kThreads - 1) / kThreads;
   if (chunks > 64) chunks = 64;  // each work-group then loops over its chunk stride
   const int64_t grid = (int64_t)num_pairs * 2 * chunks;
-  copy_blocks_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      (u32x4*)k_cache, (u32x4*)v_cache, pairs, num_blocks, block_vecs, (int)chunks);
+  move_blocks_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+      (u32x4*)dst_k, (u32x4*)dst_v, dst_blocks, (const u32x4*)src_k, (const u32x4*)src_v,
+      src_blocks, pairs, block_vecs, (int)chunks);
   return hipGetLastError();
 }
 

@@ -2,7 +2,8 @@
 // planning (kernel, partition size, grid, workspace) and kernel dispatch.
 // Every check on host-side arguments runs before anything is launched; the
 // only HIP calls before a launch are the device and compute-unit queries of
-// the stream kernel's plan.
+// the stream kernel's plan and the pointer-attribute queries of the block
+// swap.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -157,6 +158,34 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32
 }
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Where a pointer's memory lives, and the address a kernel uses for it.
+enum Residency { kUnknown, kDevice, kPinnedHost };
+Residency residency(const void* ptr, const void** kernel_ptr) {
+  hipPointerAttribute_t a;
+  if (ptr == nullptr || hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of a failed query
+    return kUnknown;
+  }
+  if (a.type == hipMemoryTypeDevice) {
+    *kernel_ptr = ptr;
+    return kDevice;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer != nullptr && a.hostPointer != nullptr) {
+    // the mapping must also be what the runtime hands out for this address
+    const void* mapped =
+        (const char*)a.devicePointer + ((const char*)ptr - (const char*)a.hostPointer);
+    void* check = nullptr;
+    if (hipHostGetDevicePointer(&check, const_cast<void*>(ptr), 0) != hipSuccess ||
+        check != mapped) {
+      (void)hipGetLastError();
+      return kUnknown;
+    }
+    *kernel_ptr = mapped;
+    return kPinnedHost;
+  }
+  return kUnknown;  // pageable host memory or a type a kernel cannot address
+}
 
 }  // namespace
 
@@ -363,8 +392,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_mapping, 8))
     return PA_ERR_INVALID_ARG;
   if ((int64_t)num_pairs * 2 * 64 > INT32_MAX) return PA_ERR_INVALID_ARG;
-  return from_hip(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_blocks,
-                                         block_bytes, (hipStream_t)stream));
+  return from_hip(pa::launch_move_blocks(k_cache, v_cache, num_blocks, k_cache, v_cache,
+                                         num_blocks, block_mapping, num_pairs, block_bytes,
+                                         (hipStream_t)stream));
 }
 
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -413,6 +443,32 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
   p.q_tiles = (int32_t)q_tiles;
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   return from_hip(pa::launch_prefill_mfma(p, head_dim, (hipStream_t)stream));
+}
+
+pa_status pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const void* src_k,
+                         const void* src_v, int64_t src_num_blocks, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t kv_heads, int32_t block_size,
+                         int32_t head_dim, int32_t dtype, void* stream) {
+  if (num_pairs < 0 || dst_num_blocks <= 0 || src_num_blocks <= 0 || kv_heads <= 0 ||
+      block_size <= 0 || head_dim <= 0 || !dtype_ok(dtype))
+    return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes = (int64_t)kv_heads * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if ((int64_t)num_pairs * 2 * 64 > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const void* p[5] = {dst_k, dst_v, src_k, src_v, block_mapping};
+  const void* kp[5];
+  Residency r[5];
+  for (int i = 0; i < 5; ++i) {
+    r[i] = residency(p[i], &kp[i]);
+    if (r[i] == kUnknown || !aligned(kp[i], i == 4 ? 8 : 16)) return PA_ERR_INVALID_ARG;
+  }
+  // the two caches of a pool live together; host-to-host moves are not GPU work
+  if (r[0] != r[1] || r[2] != r[3]) return PA_ERR_INVALID_ARG;
+  if (r[0] == kPinnedHost && r[2] == kPinnedHost) return PA_ERR_UNSUPPORTED;
+  return from_hip(pa::launch_move_blocks((void*)kp[0], (void*)kp[1], dst_num_blocks, kp[2], kp[3],
+                                         src_num_blocks, (const int64_t*)kp[4], num_pairs,
+                                         block_bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -164,8 +164,9 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
                             const int64_t* slots, int num_tokens, int64_t num_blocks,
                             int kv_heads, int block_size, int row_bytes, hipStream_t stream);
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
-                              int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
+hipError_t launch_move_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, const void* src_k,
+                              const void* src_v, int64_t src_blocks, const int64_t* pairs,
+                              int num_pairs, int64_t block_bytes, hipStream_t stream);
 
 // is_bf16: element type of q/out/caches; head_dim in {64, 128}; group in {1,2,4,8}.
 // Rows of (position, query head) one prefill work-group covers.

@@ -66,12 +66,14 @@ _decode_append = _sig("pa_decode_append", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _v
                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32,
                       _vp)
 _copy_blocks = _sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
+_swap_blocks = _sig("pa_swap_blocks", _i32, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
+                    _i32, _i32, _vp)
 _prefill = _sig("pa_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                 _i32, _i32, _i32, _i32, _f32, _i32, _vp)
 
 EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_append",
             "pa_decode_plan", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_ex",
-            "pa_decode_append", "pa_copy_blocks", "pa_prefill"]
+            "pa_decode_append", "pa_copy_blocks", "pa_prefill", "pa_swap_blocks"]
 
 
 def abi_version() -> int:
@@ -287,3 +289,38 @@ def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale, max
                   d, bs, nb, float(scale), dt, _stream(stream))
     _check(st, "prefill")
     return out
+
+
+def _ptr_any(t: torch.Tensor, name: str, dtype=None, ndim=None) -> int:
+    """Address of a device tensor or of a pinned host tensor."""
+    if not isinstance(t, torch.Tensor) or not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None) -> None:
+    """Copy whole blocks between pools: device <-> pinned host, or device <-> device.
+
+    Pools are [num_blocks, kv_heads, block_size, head_dim] of one dtype and
+    block shape; ``block_mapping`` is int64 [num_pairs, 2] (src, dst), on the
+    device or pinned.
+    """
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("pools must share the block shape")
+    if len({dst_k.dtype, dst_v.dtype, src_k.dtype, src_v.dtype}) != 1:
+        raise ValueError("pools must share a dtype")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    _, hkv, bs, d = src_k.shape
+    st = _swap_blocks(_ptr_any(dst_k, "dst_k", ndim=4), _ptr_any(dst_v, "dst_v", ndim=4),
+                      dst_k.shape[0], _ptr_any(src_k, "src_k", ndim=4),
+                      _ptr_any(src_v, "src_v", ndim=4), src_k.shape[0],
+                      _ptr_any(block_mapping, "block_mapping", torch.int64), block_mapping.shape[0],
+                      hkv, bs, d, _dtype_code(src_k), _stream(stream))
+    _check(st, "swap_blocks")

@@ -196,3 +196,24 @@ def test_prefill_host_validation(built_lib):
     assert call(B=1 << 20, hkv=2, maxq=1 << 20, T=1 << 20) == INVALID
     for empty in (dict(B=0), dict(T=0), dict(maxq=0)):
         assert call(**empty) == 0                     # nothing to do, nothing launched
+
+
+def test_swap_host_validation(built_lib):
+    """Size checks first; then every pointer's residency is queried, and
+    memory no kernel can reach (here: made-up addresses) is refused."""
+    lib = ctypes.CDLL(built_lib)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    fake = vp(4096)
+    fn = lib.pa_swap_blocks
+    fn.restype = ctypes.c_int32
+
+    def call(n=1, dnb=8, snb=8, hkv=2, bs=16, d=64, dt=1):
+        return fn(fake, fake, i64(dnb), fake, fake, i64(snb), fake, i32(n), i32(hkv), i32(bs),
+                  i32(d), i32(dt), None)
+
+    assert call(n=-1) == 1
+    assert call(dnb=0) == 1
+    assert call(dt=3) == 1
+    assert call(hkv=1, bs=1, d=3, dt=1) == 2        # 6-byte blocks
+    assert call(n=0) == 0
+    assert call() == 1                              # addresses no kernel can reach

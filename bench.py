@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama70b",
                     help="llama70b | shared_prefix | long_context | sweep_b{16,32,64}_d{64,128} "
-                         "| prefill_llama70b | prefill_chunked (one pa_prefill launch per step)")
+                         "| prefill_llama70b | prefill_chunked (one pa_prefill launch per step) "
+                         "| swap_llama70b (block swap to pinned host memory and back)")
     ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled over steps")
     ap.add_argument("--partition", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "valu"])
@@ -277,6 +278,89 @@ def prefill_main(args, np, torch, W, pa, dev):
     print(json.dumps(line), flush=True)
 
 
+SWAP_METRIC = "KV block swap for preemption: GB/s over the host link (device->host, host->device), 1 GPU"
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, per direction
+
+
+def swap_main(args, np, torch, W, pa, dev):
+    """Preempt 32 sequences of 850 tokens (the pages' 600 + 250 request, 54
+    blocks each) on the 70B layer shape: their blocks go to a pinned host pool
+    and come back into other device blocks.  Each direction is one
+    pa_swap_blocks launch, timed separately."""
+    rng = np.random.default_rng(0)
+    seqs, blocks_per_seq = 32, 54
+    n = seqs * blocks_per_seq
+    shape = (8, 16, 128)
+    dev_blocks = 2 * n + 64
+    dk = torch.empty((dev_blocks,) + shape, dtype=torch.bfloat16, device=dev)
+    dv = torch.empty_like(dk)
+    g = torch.Generator(device=dev).manual_seed(0)
+    dk.normal_(generator=g)
+    dv.normal_(generator=g)
+    hk = torch.empty((n,) + shape, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    perm = rng.permutation(dev_blocks)
+    out_pairs = torch.from_numpy(np.stack([perm[:n], rng.permutation(n)], 1).astype(np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), perm[n:2 * n]], 1).astype(np.int64)).to(dev)
+    bytes_moved = 2 * n * int(np.prod(shape)) * 2
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        timer = HipTimer()
+        a, b = timer.event(), timer.event()
+        timer.record(a, stream)
+        for _ in range(args.steps):
+            fn()
+        timer.record(b, stream)
+        torch.cuda.synchronize()
+        ms = timer.elapsed_ms(a, b) / args.steps
+        timer.close()
+        return ms
+
+    out_ms = timed(lambda: pa.swap_blocks(hk, hv, dk, dv, out_pairs))
+    in_ms = timed(lambda: pa.swap_blocks(dk, dv, hk, hv, in_pairs))
+    # context: one contiguous DMA copy of the same bytes each way
+    flat_d = torch.empty(bytes_moved // 2, dtype=torch.bfloat16, device=dev)
+    flat_h = torch.empty(bytes_moved // 2, dtype=torch.bfloat16, pin_memory=True)
+    dma_out_ms = timed(lambda: flat_h.copy_(flat_d, non_blocking=True))
+    dma_in_ms = timed(lambda: flat_d.copy_(flat_h, non_blocking=True))
+    out_gbs = bytes_moved / (out_ms * 1e-3) / 1e9
+    in_gbs = bytes_moved / (in_ms * 1e-3) / 1e9
+    total_gbs = 2 * bytes_moved / ((out_ms + in_ms) * 1e-3) / 1e9
+    line = {
+        "metric": SWAP_METRIC,
+        "value": round(total_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(out_ms + in_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "swap_llama70b", "preempted_seqs": seqs,
+                   "blocks_per_seq": blocks_per_seq, "blocks": n, "kv_heads": 8,
+                   "block_size": 16, "head_dim": 128, "parallelism": "single GPU"},
+        "bytes_per_direction": bytes_moved,
+        "device_to_host": {"ms": round(out_ms, 5), "GBps": round(out_gbs, 2)},
+        "host_to_device": {"ms": round(in_ms, 5), "GBps": round(in_gbs, 2)},
+        "contiguous_dma_copy": {"device_to_host_GBps": round(bytes_moved / (dma_out_ms * 1e-3) / 1e9, 2),
+                                "host_to_device_GBps": round(bytes_moved / (dma_in_ms * 1e-3) / 1e9, 2)},
+        "roofline": {"bound": "host_link", "achieved": round(total_gbs, 2),
+                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(total_gbs / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "move_blocks_kernel", "bytes_per_launch": bytes_moved,
+                     "avg_launch_ms": round((out_ms + in_ms) / 2, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -299,6 +383,8 @@ def main():
 
     if args.workload in W.PREFILL_WORKLOADS:
         return prefill_main(args, np, torch, W, pa, dev)
+    if args.workload == "swap_llama70b":
+        return swap_main(args, np, torch, W, pa, dev)
 
     if args.copy_calibration:
         n = 1 << 30

@@ -37,7 +37,9 @@
  *                       convention as the explainer's block_layout, which
  *                       rejects negative sizes);
  *   PA_ERR_UNSUPPORTED  a shape with no kernel instance (see each call);
- *   PA_ERR_HIP          the HIP runtime reported a launch error.
+ *   PA_ERR_HIP          the HIP runtime reported a launch error;
+ *   PA_ERR_NO_SPACE     (block manager) the pool cannot cover the request:
+ *                       wait, or preempt a sequence; nothing changed.
  * On an error nothing has been launched (PA_ERR_HIP: possibly part of it).
  * Device-resident contents (table entries, slots, lengths) are read by the
  * kernels, which never access memory outside the arrays described here:
@@ -57,7 +59,8 @@ typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1,
   PA_ERR_UNSUPPORTED = 2,
-  PA_ERR_HIP = 3
+  PA_ERR_HIP = 3,
+  PA_ERR_NO_SPACE = 4
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -319,6 +322,67 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const
                          const void* src_v, int64_t src_num_blocks, const int64_t* block_mapping,
                          int32_t num_pairs, int32_t kv_heads, int32_t block_size,
                          int32_t head_dim, int32_t dtype, void* stream);
+
+/*
+ * Block manager: the host-side bookkeeping around the kernels (plain C++, no
+ * GPU calls).  It owns the free lists and reference counts of a device pool
+ * of num_blocks blocks and a pinned-host pool of num_host_blocks, the block
+ * table and cached length of every sequence, and hands out what the kernel
+ * calls take: slots for pa_kv_append, (src, dst) pairs for pa_copy_blocks
+ * and pa_swap_blocks, block-table rows and lengths for pa_decode.
+ *
+ *   admission   ("How PagedAttention works", section "What interviewers probe
+ *               next") a prompt of T tokens is admitted when
+ *               free - watermark >= ceil(T / block_size) + 1; it takes
+ *               ceil(T / block_size) blocks;
+ *   sharing     (same page, "A strong answer" feature table) fork gives the
+ *               child every block of the parent (reference counts + 1); an
+ *               append into a shared, partly filled last block first takes a
+ *               private copy (copy on write: the (shared, copy) pair goes to
+ *               pa_copy_blocks and the shared block loses one reference);
+ *               release drops one reference per block;
+ *   preemption  (same table) swap-out moves a sequence's blocks to host
+ *               blocks, swap-in to fresh device blocks; the pairs go to
+ *               pa_swap_blocks.
+ * Policies: the lowest-numbered free block is taken first; the watermark
+ * gates admission only; a batch of appends is all or nothing; a swapped-out
+ * sequence cannot grow, fork or be decoded.  Sequence ids are any int64.
+ * Errors: unknown or duplicate ids, a swapped-out sequence where a resident
+ * one is needed, NULL outputs, too small output capacities ->
+ * PA_ERR_INVALID_ARG; too few free blocks -> PA_ERR_NO_SPACE.  On any error
+ * the manager is unchanged.  Not thread-safe: serialise calls on one manager.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+pa_status pa_bm_create(int64_t num_blocks, int32_t block_size, int64_t watermark_blocks,
+                       int64_t num_host_blocks, pa_block_manager** out);
+pa_status pa_bm_destroy(pa_block_manager* bm);
+/* *ok = 1 when a prompt of prompt_tokens tokens can be admitted now. */
+pa_status pa_bm_can_admit(const pa_block_manager* bm, int64_t prompt_tokens, int32_t* ok);
+pa_status pa_bm_admit(pa_block_manager* bm, int64_t seq, int64_t prompt_tokens);
+pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+/* Reserve the next token's slot of each of the n (distinct, resident) seqs:
+ * slots[i] for pa_kv_append; cow_pairs (capacity n pairs, int64 (src, dst))
+ * receives *num_cow copy-on-write pairs for pa_copy_blocks, in batch order. */
+pa_status pa_bm_append_slots(pa_block_manager* bm, const int64_t* seqs, int32_t n,
+                             int64_t* slots, int64_t* cow_pairs, int32_t* num_cow);
+pa_status pa_bm_release(pa_block_manager* bm, int64_t seq);
+/* pairs: capacity entries of int64 (device, host) (swap-out) or (host, device)
+ * (swap-in), one per block of the sequence, in table order. */
+pa_status pa_bm_swap_out(pa_block_manager* bm, int64_t seq, int64_t* pairs, int64_t capacity,
+                         int64_t* num_pairs);
+pa_status pa_bm_swap_in(pa_block_manager* bm, int64_t seq, int64_t* pairs, int64_t capacity,
+                        int64_t* num_pairs);
+/* Host buffers: tables [n][max_blocks] (rows padded with pad_block), seq_lens [n]. */
+pa_status pa_bm_decode_inputs(const pa_block_manager* bm, const int64_t* seqs, int32_t n,
+                              int32_t max_blocks, int32_t pad_block, int32_t* tables,
+                              int32_t* seq_lens);
+pa_status pa_bm_sequence(const pa_block_manager* bm, int64_t seq, int64_t* len,
+                         int64_t* num_blocks, int32_t* swapped);
+pa_status pa_bm_stats(const pa_block_manager* bm, int64_t* free_blocks, int64_t* free_host_blocks,
+                      int64_t* num_seqs);
+/* Reference count of a device (host = 0) or host (host = 1) block. */
+pa_status pa_bm_refcount(const pa_block_manager* bm, int64_t block, int32_t host, int32_t* ref);
 
 #ifdef __cplusplus
 }

@@ -142,6 +142,8 @@ class BlockManager:
 
     # -- release and preemption -------------------------------------------------
     def release(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise ValueError("unknown sequence")
         pool = self.host if seq in self.swapped else self.dev
         for blk in self.tables.pop(seq):
             pool.drop(blk)

@@ -2,7 +2,8 @@
 
     python -m paged_kv_cache_163_amd.build
 
-Each ``csrc/*.hip`` is compiled to an object in parallel, then linked into
+Each ``csrc/*.hip`` is compiled with hipcc and each host-only ``csrc/*.cpp``
+with the host C++ compiler, in parallel, then linked into
 ``paged_kv_cache_163_amd/libpa.so`` (written atomically).  hipcc
 cross-compiles for gfx950 without a GPU present.
 """
@@ -39,8 +40,21 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
+def cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler (set CXX)")
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [cxx(), *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    else:
+        cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -48,8 +62,8 @@ def _compile(src: str, obj: str) -> None:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
     workers = max(1, min(len(srcs), os.cpu_count() or 1, 8))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         list(ex.map(_compile, srcs, objs))

@@ -279,6 +279,7 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_INVALID_ARG: return "invalid argument";
     case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PA_ERR_HIP: return "HIP launch error";
+    case PA_ERR_NO_SPACE: return "not enough free blocks";
     default: return "unknown status";
   }
 }

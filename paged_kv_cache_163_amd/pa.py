@@ -35,7 +35,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, 1, 2, 3
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_SPACE = 0, 1, 2, 3, 4
 PA_F32, PA_BF16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "stream": 3}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
@@ -66,6 +66,21 @@ _decode_append = _sig("pa_decode_append", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _v
                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32,
                       _vp)
 _copy_blocks = _sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
+_P = ctypes.POINTER
+_bm_create = _sig("pa_bm_create", _i32, _i64, _i32, _i64, _i64, _P(_vp))
+_bm_destroy = _sig("pa_bm_destroy", _i32, _vp)
+_bm_can_admit = _sig("pa_bm_can_admit", _i32, _vp, _i64, _P(_i32))
+_bm_admit = _sig("pa_bm_admit", _i32, _vp, _i64, _i64)
+_bm_fork = _sig("pa_bm_fork", _i32, _vp, _i64, _i64)
+_bm_append_slots = _sig("pa_bm_append_slots", _i32, _vp, _P(_i64), _i32, _P(_i64), _P(_i64), _P(_i32))
+_bm_release = _sig("pa_bm_release", _i32, _vp, _i64)
+_bm_swap_out = _sig("pa_bm_swap_out", _i32, _vp, _i64, _P(_i64), _i64, _P(_i64))
+_bm_swap_in = _sig("pa_bm_swap_in", _i32, _vp, _i64, _P(_i64), _i64, _P(_i64))
+_bm_decode_inputs = _sig("pa_bm_decode_inputs", _i32, _vp, _P(_i64), _i32, _i32, _i32, _P(_i32),
+                         _P(_i32))
+_bm_sequence = _sig("pa_bm_sequence", _i32, _vp, _i64, _P(_i64), _P(_i64), _P(_i32))
+_bm_stats = _sig("pa_bm_stats", _i32, _vp, _P(_i64), _P(_i64), _P(_i64))
+_bm_refcount = _sig("pa_bm_refcount", _i32, _vp, _i64, _i32, _P(_i32))
 _swap_blocks = _sig("pa_swap_blocks", _i32, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                     _i32, _i32, _vp)
 _prefill = _sig("pa_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -73,7 +88,10 @@ _prefill = _sig("pa_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i3
 
 EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_append",
             "pa_decode_plan", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_ex",
-            "pa_decode_append", "pa_copy_blocks", "pa_prefill", "pa_swap_blocks"]
+            "pa_decode_append", "pa_copy_blocks", "pa_prefill", "pa_swap_blocks",
+            "pa_bm_create", "pa_bm_destroy", "pa_bm_can_admit", "pa_bm_admit", "pa_bm_fork",
+            "pa_bm_append_slots", "pa_bm_release", "pa_bm_swap_out", "pa_bm_swap_in",
+            "pa_bm_decode_inputs", "pa_bm_sequence", "pa_bm_stats", "pa_bm_refcount"]
 
 
 def abi_version() -> int:
@@ -88,7 +106,13 @@ def _check(status: int, what: str) -> None:
         raise ValueError(msg)
     if status == PA_ERR_UNSUPPORTED:
         raise NotImplementedError(msg)
+    if status == PA_ERR_NO_SPACE:
+        raise NoSpace(msg)
     raise RuntimeError(msg)
+
+
+class NoSpace(MemoryError):
+    """The block pool cannot cover the request (PA_ERR_NO_SPACE): wait or preempt."""
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -324,3 +348,101 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None) -> None:
                       _ptr_any(block_mapping, "block_mapping", torch.int64), block_mapping.shape[0],
                       hkv, bs, d, _dtype_code(src_k), _stream(stream))
     _check(st, "swap_blocks")
+
+
+class BlockManager:
+    """Host block bookkeeping (pa_bm_*): admission, sharing, copy-on-write,
+    swap, and the decode inputs.  Raises NoSpace when the pool is short."""
+
+    def __init__(self, num_blocks: int, block_size: int, watermark: int = 0,
+                 num_host_blocks: int = 0):
+        h = _vp()
+        _check(_bm_create(int(num_blocks), int(block_size), int(watermark), int(num_host_blocks),
+                          ctypes.byref(h)), "bm_create")
+        self._h = h
+        self._destroy = _bm_destroy   # kept for interpreter shutdown, when globals are gone
+        self.block_size = int(block_size)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def can_admit(self, prompt_tokens: int) -> bool:
+        ok = _i32()
+        _check(_bm_can_admit(self._h, int(prompt_tokens), ctypes.byref(ok)), "bm_can_admit")
+        return bool(ok.value)
+
+    def admit(self, seq: int, prompt_tokens: int) -> None:
+        _check(_bm_admit(self._h, int(seq), int(prompt_tokens)), "bm_admit")
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(_bm_fork(self._h, int(parent), int(child)), "bm_fork")
+
+    def append_slots(self, seqs):
+        """Returns (slots, cow_pairs) as lists (slots in batch order)."""
+        seqs = [int(x) for x in seqs]
+        n = len(seqs)
+        arr = (_i64 * max(n, 1))(*seqs)
+        slots = (_i64 * max(n, 1))()
+        cow = (_i64 * max(2 * n, 2))()
+        ncow = _i32()
+        _check(_bm_append_slots(self._h, arr, n, slots, cow, ctypes.byref(ncow)), "bm_append_slots")
+        return list(slots[:n]), [(cow[2 * i], cow[2 * i + 1]) for i in range(ncow.value)]
+
+    def release(self, seq: int) -> None:
+        _check(_bm_release(self._h, int(seq)), "bm_release")
+
+    def _swap(self, fn, seq, what):
+        _, nblocks, _ = self.sequence(seq)
+        pairs = (_i64 * max(2 * nblocks, 2))()
+        n = _i64()
+        _check(fn(self._h, int(seq), pairs, nblocks, ctypes.byref(n)), what)
+        return [(pairs[2 * i], pairs[2 * i + 1]) for i in range(n.value)]
+
+    def swap_out(self, seq: int):
+        """(device, host) block pairs for pa_swap_blocks."""
+        return self._swap(_bm_swap_out, seq, "bm_swap_out")
+
+    def swap_in(self, seq: int):
+        """(host, device) block pairs for pa_swap_blocks."""
+        return self._swap(_bm_swap_in, seq, "bm_swap_in")
+
+    def decode_inputs(self, seqs, max_blocks: int, pad_block: int):
+        """(tables [n][max_blocks], seq_lens [n]) as nested lists."""
+        seqs = [int(x) for x in seqs]
+        n = len(seqs)
+        arr = (_i64 * max(n, 1))(*seqs)
+        tables = (_i32 * max(n * max_blocks, 1))()
+        lens = (_i32 * max(n, 1))()
+        _check(_bm_decode_inputs(self._h, arr, n, int(max_blocks), int(pad_block), tables, lens),
+               "bm_decode_inputs")
+        return ([list(tables[i * max_blocks:(i + 1) * max_blocks]) for i in range(n)],
+                list(lens[:n]))
+
+    def sequence(self, seq: int):
+        """(cached length, number of blocks, swapped out?)"""
+        ln, nb, sw = _i64(), _i64(), _i32()
+        _check(_bm_sequence(self._h, int(seq), ctypes.byref(ln), ctypes.byref(nb),
+                            ctypes.byref(sw)), "bm_sequence")
+        return ln.value, nb.value, bool(sw.value)
+
+    def stats(self):
+        """(free device blocks, free host blocks, sequences)"""
+        a, b, c = _i64(), _i64(), _i64()
+        _check(_bm_stats(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "bm_stats")
+        return a.value, b.value, c.value
+
+    def free_blocks(self) -> int:
+        return self.stats()[0]
+
+    def free_host_blocks(self) -> int:
+        return self.stats()[1]
+
+    def refcount(self, block: int, host: bool = False) -> int:
+        r = _i32()
+        _check(_bm_refcount(self._h, int(block), int(host), ctypes.byref(r)), "bm_refcount")
+        return r.value

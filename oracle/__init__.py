@@ -34,7 +34,9 @@ from .paged_attention import (  # noqa: F401
     gather_history,
     gather_history_vectorised,
     kv_append,
+    layer_views,
     paged_decode,
+    paged_decode_layered,
     paged_prefill,
     swap_blocks,
     to_f64,

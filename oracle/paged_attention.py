@@ -189,6 +189,49 @@ def contiguous_decode(q, keys_per_seq, values_per_seq, scale: float) -> np.ndarr
 
 
 # --------------------------------------------------------------------------
+# Layered pool: every layer's K and V in one block
+# --------------------------------------------------------------------------
+
+def layer_views(kv_pool, layer: int):
+    """The per-layer K and V caches ``[num_blocks, kv_heads, block_size,
+    head_dim]`` inside a layered pool ``[num_blocks, 2, num_layers, kv_heads,
+    block_size, head_dim]`` (zenaique.com code box "Conceptual:
+    PagedAttention block lookup": index 0 of the second axis holds K, 1 holds
+    V).  numpy views: writes go to the pool."""
+    return kv_pool[:, 0, layer], kv_pool[:, 1, layer]
+
+
+def paged_decode_layered(q_layers, kv_pool, block_tables, seq_lens, scale: float,
+                         block_size: int, layers=None, seqs=None) -> np.ndarray:
+    """Decode attention of several layers over one layered pool.
+
+    ``q_layers`` ``[num_layers, num_seqs, num_heads, head_dim]``.  Follows the
+    zenaique.com code box: for each position, the physical block and offset
+    come from the sequence's block table, and one lookup
+    ``kv_pool[block, 0 or 1, :, :, offset, :]`` fetches that position's K (or
+    V) for every layer and KV head at once; each layer then runs the same
+    scaled dot-product attention as :func:`attend`.  Returns float64
+    ``[len(layers), len(seqs), num_heads, head_dim]``.
+    """
+    q_layers = np.asarray(q_layers)
+    num_layers = kv_pool.shape[2]
+    layers = list(range(num_layers)) if layers is None else list(layers)
+    seqs = list(range(q_layers.shape[1])) if seqs is None else list(seqs)
+    out = np.empty((len(layers), len(seqs), q_layers.shape[2], q_layers.shape[3]), dtype=np.float64)
+    for j, s in enumerate(seqs):
+        seq_len = int(seq_lens[s])
+        keys = np.empty((seq_len, num_layers) + kv_pool.shape[3:4] + kv_pool.shape[5:6])
+        values = np.empty_like(keys)
+        for position in range(seq_len):
+            block, slot = translate(block_tables[s], position, block_size)
+            keys[position] = to_f64(kv_pool[block, 0, :, :, slot, :])
+            values[position] = to_f64(kv_pool[block, 1, :, :, slot, :])
+        for i, layer in enumerate(layers):
+            out[i, j] = attend(to_f64(q_layers[layer, s]), keys[:, layer], values[:, layer], scale)
+    return out
+
+
+# --------------------------------------------------------------------------
 # Prefill: a chunk of queries per sequence, causal
 # --------------------------------------------------------------------------
 

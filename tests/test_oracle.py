@@ -438,6 +438,50 @@ def pin_swap_round_trip():
     return np.array_equal(a_k, b_k) and np.array_equal(a_v, b_v)
 
 
+def _layered_pool(rng, lens, layers, hkv, d, bs):
+    """A layered pool [NB, 2, L, Hkv, b, D] and, for every layer, the same data
+    as a separate per-layer batch (shared tables)."""
+    per_layer = []
+    tables = None
+    for _ in range(layers):
+        q, kc, vc, tables_l, _, _ = _random_paged_batch(np.random.default_rng(rng.integers(1 << 30)),
+                                                        lens, 2 * hkv, hkv, d, bs)
+        if tables is None:
+            tables = tables_l
+            nb = kc.shape[0]
+        # same physical placement for every layer: re-scatter through layer 0's table
+        kc0 = np.full_like(kc, np.nan)
+        vc0 = np.full_like(vc, np.nan)
+        for s, n in enumerate(lens):
+            for t in range(n):
+                bsrc, off = oracle.translate(tables_l[s], t, bs)
+                bdst, _ = oracle.translate(tables[s], t, bs)
+                kc0[bdst, :, off] = kc[bsrc, :, off]
+                vc0[bdst, :, off] = vc[bsrc, :, off]
+        per_layer.append((q, kc0, vc0))
+    pool = np.stack([np.stack([kc for _, kc, _ in per_layer], 1),
+                     np.stack([vc for _, _, vc in per_layer], 1)], 1)
+    return pool, tables, per_layer, nb
+
+
+def pin_layered_equals_per_layer():
+    """The code box's all-layer lookup on a layered pool gives, layer by layer,
+    exactly the per-layer decode over that layer's own pool; layer_views are
+    those per-layer pools."""
+    rng = np.random.default_rng(51)
+    lens = [9, 1, 17]
+    pool, tables, per_layer, _ = _layered_pool(rng, lens, 3, 2, 8, 4)
+    q_layers = np.stack([q for q, _, _ in per_layer])
+    out = oracle.paged_decode_layered(q_layers, pool, tables, lens, 0.3, 4)
+    for layer, (q, kc, vc) in enumerate(per_layer):
+        if not np.array_equal(out[layer], oracle.paged_decode(q, kc, vc, tables, lens, 0.3, 4)):
+            return False
+        kv, vv = oracle.layer_views(pool, layer)
+        if not (np.array_equal(kv, kc, equal_nan=True) and np.array_equal(vv, vc, equal_nan=True)):
+            return False
+    return True
+
+
 ALL_PINS = [
     pin_block_layout_golden, pin_block_layout_bounds, pin_translation_golden,
     pin_paged_equals_contiguous, pin_single_token, pin_equal_keys_mean,
@@ -446,6 +490,7 @@ ALL_PINS = [
     pin_shared_prefix_equals_private, pin_append_roundtrip, pin_copy_blocks, pin_bf16_decode,
     pin_prefill_single_query_is_decode, pin_prefill_torch_sdpa_causal,
     pin_prefill_chunk_rows_of_full, pin_prefill_future_keys_ignored, pin_swap_round_trip,
+    pin_layered_equals_per_layer,
 ]
 
 
@@ -580,6 +625,21 @@ def _swap_keys_only(dst_k, dst_v, src_k, src_v, pairs):
         dst_k[dst] = src_k[src]
 
 
+def _layer_views_kv_swapped(kv_pool, layer):
+    return kv_pool[:, 1, layer], kv_pool[:, 0, layer]
+
+
+def _layer_views_wrong_axis(kv_pool, layer):
+    return kv_pool[:, 0, :, layer % kv_pool.shape[3]], kv_pool[:, 1, :, layer % kv_pool.shape[3]]
+
+
+def _layered_kv_swapped(q_layers, kv_pool, block_tables, seq_lens, scale, block_size,
+                        layers=None, seqs=None):
+    flipped = kv_pool[:, ::-1]
+    return opa.__dict__["_orig_layered"](q_layers, flipped, block_tables, seq_lens, scale,
+                                         block_size, layers, seqs)
+
+
 PLANTED = {
     "attend": [_attend_wrong_gqa, _attend_no_scale, _attend_no_max_shift, _attend_kv_swapped,
                _attend_drop_last],
@@ -588,6 +648,8 @@ PLANTED = {
     "chunk_positions": [_positions_from_zero],
     "visible_prefix": [_visible_exclusive, _visible_all],
     "swap_blocks": [_swap_reversed, _swap_keys_only],
+    "layer_views": [_layer_views_kv_swapped, _layer_views_wrong_axis],
+    "paged_decode_layered": [_layered_kv_swapped],
 }
 
 
@@ -605,6 +667,7 @@ def _any_pin_fails():
                          ids=lambda x: getattr(x, "__name__", str(x)))
 def test_planted_mistake_is_caught(monkeypatch, target, bad):
     monkeypatch.setitem(opa.__dict__, "_orig_attend", opa.attend)
+    monkeypatch.setitem(opa.__dict__, "_orig_layered", opa.paged_decode_layered)
     monkeypatch.setattr(opa, target, bad)
     monkeypatch.setattr(oracle, target, bad)
     assert _any_pin_fails(), f"no pin caught the planted mistake {bad.__name__}"

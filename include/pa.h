@@ -324,6 +324,53 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const
                          int32_t head_dim, int32_t dtype, void* stream);
 
 /*
+ * Layered pool: one pool for every layer, [num_blocks][2][num_layers]
+ * [kv_heads][block_size][head_dim] -- a block holds the K (index 0) and V
+ * (index 1) of all layers for its block_size tokens (zenaique.com code box
+ * "Conceptual: PagedAttention block lookup"; "How PagedAttention works",
+ * section "A strong answer": one pool per layer or a layered layout).  One
+ * block table per sequence serves every layer; slots and block ids mean the
+ * same as for per-layer pools.  Same element types, shapes, errors and
+ * device-content behaviour as the per-layer calls, plus: layer indices out
+ * of [0, num_layers) -> PA_ERR_INVALID_ARG.
+ *
+ * pa_kv_append_layered   pa_kv_append of layer `layer`'s new K/V rows.
+ * pa_decode_layered      decode of layers [first_layer, first_layer + layers)
+ *                        in ONE launch (grid over layers): q and out are
+ *                        [layers][num_seqs][num_heads][head_dim]; every layer
+ *                        uses the same tables and lengths.  bf16 on the
+ *                        matrix-core kernel only (other shapes or fp32 ->
+ *                        PA_ERR_UNSUPPORTED); the workspace is `layers` times
+ *                        pa_decode_plan's for one layer.  layers <= 65535.
+ * pa_copy_blocks_layered copy-on-write of whole blocks (every layer, K and V).
+ * pa_swap_blocks_layered pa_swap_blocks of whole layered blocks between a
+ *                        device pool and a pinned-host pool (or two device
+ *                        pools); the same residency checks.
+ */
+pa_status pa_kv_append_layered(const void* k_new, const void* v_new, void* kv_pool, int32_t layer,
+                               int32_t num_layers, const int64_t* slot_mapping,
+                               int32_t num_tokens, int32_t num_blocks, int32_t kv_heads,
+                               int32_t block_size, int32_t head_dim, int32_t dtype,
+                               void* stream);
+pa_status pa_decode_layered(void* out, const void* q, const void* kv_pool, int32_t first_layer,
+                            int32_t layers, int32_t num_layers, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            int32_t max_seq_len, int32_t num_seqs, int32_t num_heads,
+                            int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float scale, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, int32_t dtype,
+                            void* stream);
+pa_status pa_copy_blocks_layered(void* kv_pool, const int64_t* block_mapping, int32_t num_pairs,
+                                 int32_t num_blocks, int32_t num_layers, int32_t kv_heads,
+                                 int32_t block_size, int32_t head_dim, int32_t dtype,
+                                 void* stream);
+pa_status pa_swap_blocks_layered(void* dst_pool, int64_t dst_num_blocks, const void* src_pool,
+                                 int64_t src_num_blocks, const int64_t* block_mapping,
+                                 int32_t num_pairs, int32_t num_layers, int32_t kv_heads,
+                                 int32_t block_size, int32_t head_dim, int32_t dtype,
+                                 void* stream);
+
+/*
  * Block manager: the host-side bookkeeping around the kernels (plain C++, no
  * GPU calls).  It owns the free lists and reference counts of a device pool
  * of num_blocks blocks and a pinned-host pool of num_host_blocks, the block

@@ -130,13 +130,18 @@ __device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_his
                 __builtin_amdgcn_readfirstlane(sm_pick[1])};
 }
 
-template <int D, bool kFused>
+// kModePlain: one per-layer pool.  kModeFused: plus the step's append.
+// kModeLayered: one or more layers of a layered pool (layer = blockIdx.y).
+enum Mode { kModePlain, kModeFused, kModeLayered };
+
+template <int D, int M>
 __global__ __launch_bounds__(kWaves * 64)
 #if PA_MFMA_MIN_WAVES_PER_EU > 0
 __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES_PER_EU)))
 #endif
 void decode_mfma_kernel(DecodeParams p) {
   constexpr int kKi = D / 32;
+  constexpr bool kFused = M == kModeFused;
   __shared__ float sm_o[kWaves][16][D];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
@@ -154,7 +159,23 @@ void decode_mfma_kernel(DecodeParams p) {
   const int G = p.group;
   const int len = rk.len;
   const int64_t out_row0 = (int64_t)w.seq * p.num_heads + (int64_t)w.head * G;
+  const char* qbase = (const char*)p.q;
+  const char* kcache = (const char*)p.k_cache;
+  const char* vcache = (const char*)p.v_cache;
   uint16_t* out = (uint16_t*)p.out;
+  float* ws_o = p.ws_o;
+  float* ws_ml = p.ws_ml;
+  if constexpr (M == kModeLayered) {
+    const int64_t layer = blockIdx.y;
+    qbase += layer * p.layer_q_stride * 2;
+    out += layer * p.layer_q_stride;
+    kcache += layer * p.layer_kv_stride * 2;
+    vcache += layer * p.layer_kv_stride * 2;
+    if (ws_o != nullptr) {
+      ws_o += layer * p.layer_ws_stride;
+      ws_ml += layer * (p.layer_ws_stride / D) * 2;
+    }
+  }
 
   if (!seq_len_ok(p, len) || len == 0) {
     if (w.part == 0) {
@@ -190,7 +211,7 @@ void decode_mfma_kernel(DecodeParams p) {
   // Q^T as the B operand: column r16 = query head h*G + r16, zero when r16 >= G.
   u32x4 qb[kKi];
   {
-    const char* qrow = (const char*)p.q + ((out_row0 + r16) * D) * 2 + q4 * 16;
+    const char* qrow = qbase + ((out_row0 + r16) * D) * 2 + q4 * 16;
 #pragma unroll
     for (int i = 0; i < kKi; ++i)
       qb[i] = r16 < G ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
@@ -198,10 +219,10 @@ void decode_mfma_kernel(DecodeParams p) {
 
   SeqView c;
   const int64_t head_stride = (int64_t)p.block_size * D * 2;
-  c.kbase = (const char*)p.k_cache + (int64_t)w.head * head_stride;
-  c.vbase = (const char*)p.v_cache + (int64_t)w.head * head_stride;
+  c.kbase = kcache + (int64_t)w.head * head_stride;
+  c.vbase = vcache + (int64_t)w.head * head_stride;
   c.table = p.block_tables + (int64_t)w.seq * p.max_blocks_per_seq;
-  c.block_stride = (int64_t)p.kv_heads * head_stride;
+  c.block_stride = M == kModeLayered ? p.block_stride * 2 : (int64_t)p.kv_heads * head_stride;
   c.nblocks_valid = (len + p.block_size - 1) >> p.block_shift;
   c.num_blocks = p.num_blocks;
   c.block_shift = p.block_shift;
@@ -250,10 +271,10 @@ void decode_mfma_kernel(DecodeParams p) {
       out[(out_row0 + g) * D + d] = f32_to_bf16(o / l);
     } else {
       const int64_t slot = (out_row0 + g) * p.num_partitions + w.part;
-      p.ws_o[slot * D + d] = o;
+      ws_o[slot * D + d] = o;
       if (d == 0) {
-        p.ws_ml[slot * 2 + 0] = mx;
-        p.ws_ml[slot * 2 + 1] = l;
+        ws_ml[slot * 2 + 0] = mx;
+        ws_ml[slot * 2 + 1] = l;
       }
     }
   }
@@ -263,19 +284,25 @@ void decode_mfma_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.num_partitions * p.num_seqs * p.kv_heads));
+  const dim3 grid((unsigned)((int64_t)p.num_partitions * p.num_seqs * p.kv_heads),
+                  (unsigned)(p.num_layers > 1 ? p.num_layers : 1));
   const dim3 block(kWaves * 64);
-  const bool fused = p.new_slots != nullptr;
-  if (head_dim == 128 && fused)
-    decode_mfma_kernel<128, true><<<grid, block, 0, stream>>>(p);
-  else if (head_dim == 128)
-    decode_mfma_kernel<128, false><<<grid, block, 0, stream>>>(p);
-  else if (head_dim == 64 && fused)
-    decode_mfma_kernel<64, true><<<grid, block, 0, stream>>>(p);
-  else if (head_dim == 64)
-    decode_mfma_kernel<64, false><<<grid, block, 0, stream>>>(p);
-  else
+  const int mode = p.block_stride != 0      ? kModeLayered
+                   : p.new_slots != nullptr ? kModeFused
+                                            : kModePlain;
+#define PA_LAUNCH(DIM, MODE) decode_mfma_kernel<DIM, MODE><<<grid, block, 0, stream>>>(p)
+  if (head_dim == 128) {
+    if (mode == kModeLayered) PA_LAUNCH(128, kModeLayered);
+    else if (mode == kModeFused) PA_LAUNCH(128, kModeFused);
+    else PA_LAUNCH(128, kModePlain);
+  } else if (head_dim == 64) {
+    if (mode == kModeLayered) PA_LAUNCH(64, kModeLayered);
+    else if (mode == kModeFused) PA_LAUNCH(64, kModeFused);
+    else PA_LAUNCH(64, kModePlain);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef PA_LAUNCH
   return hipGetLastError();
 }
 

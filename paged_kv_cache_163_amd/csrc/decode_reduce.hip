@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
   const int nparts = ceil_div_i(len, p.partition_size);
   if (nparts <= 1) return;          // written directly by the partition kernel
   const int64_t slot0 = ((int64_t)seq * p.num_heads + hq) * p.num_partitions;
-  const float* ml = p.ws_ml + slot0 * 2;
+  const int64_t layer = blockIdx.y;  // layered pool: one grid row per decoded layer
+  const float* ml = p.ws_ml + layer * (p.layer_ws_stride / D) * 2 + slot0 * 2;
 
   float mx = -INFINITY;
   for (int q = threadIdx.x; q < nparts; q += kThreads) mx = fmaxf(mx, ml[2 * q]);
@@ -60,12 +61,12 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
   }
   l = block_sum(l, red);  // its barriers also publish sm_w
   const float inv = 1.0f / l;
-  const float* o = p.ws_o + slot0 * D;
+  const float* o = p.ws_o + layer * p.layer_ws_stride + slot0 * D;
   for (int d = threadIdx.x; d < D; d += kThreads) {
     float acc = 0.f;
     for (int q = 0; q < nparts; ++q) acc += sm_w[q] * o[(int64_t)q * D + d];
     const float r = acc * inv;
-    const int64_t idx = ((int64_t)seq * p.num_heads + hq) * D + d;
+    const int64_t idx = layer * p.layer_q_stride + ((int64_t)seq * p.num_heads + hq) * D + d;
     if (BF16)
       ((uint16_t*)p.out)[idx] = f32_to_bf16(r);
     else
@@ -75,7 +76,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
 
 template <bool BF16, int D>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_heads));
+  const dim3 grid((unsigned)((int64_t)p.num_seqs * p.num_heads),
+                  (unsigned)(p.num_layers > 1 ? p.num_layers : 1));
   const size_t lds = (size_t)p.num_partitions * sizeof(float);
   decode_reduce_kernel<BF16, D><<<grid, kThreads, lds, stream>>>(p);
   return hipGetLastError();

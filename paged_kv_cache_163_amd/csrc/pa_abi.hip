@@ -189,6 +189,14 @@ Residency residency(const void* ptr, const void** kernel_ptr) {
 
 }  // namespace
 
+// Decode over layers of a layered pool: k_cache / v_cache point at the first
+// decoded layer, `layers` layers are decoded by one launch.
+struct LayerSpec {
+  int64_t block_stride;     // elements between physical blocks
+  int64_t layer_kv_stride;  // elements between consecutive layers' K (and V)
+  int32_t layers;
+};
+
 static pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, int32_t max_blocks_per_seq,
                              const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
@@ -196,11 +204,16 @@ static pa_status decode_impl(void* out, const void* q, const void* k_cache, cons
                              int32_t block_size, int32_t num_blocks, float scale,
                              int32_t partition_size, void* workspace, size_t workspace_bytes,
                              int32_t dtype, int32_t kernel, void* stream, const void* k_new,
-                             const void* v_new, const int64_t* new_slots) {
+                             const void* v_new, const int64_t* new_slots,
+                             const LayerSpec* lay = nullptr) {
   Plan plan;
   const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
                                  max_seq_len, partition_size, dtype, kernel, &plan);
   if (st != PA_OK) return st;
+  if (lay != nullptr) {  // layered pools run on the matrix-core kernel only
+    if (plan.kernel != PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
+    plan.workspace *= (size_t)lay->layers;
+  }
   if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
@@ -238,8 +251,16 @@ static pa_status decode_impl(void* out, const void* q, const void* k_cache, cons
     p.num_workgroups = plan.partitions;
     p.epoch = next_epoch();
   } else if (plan.workspace > 0) {
+    const size_t per_layer_o = (size_t)num_seqs * num_heads * plan.partitions * head_dim;
     p.ws_o = (float*)workspace;
-    p.ws_ml = p.ws_o + (size_t)num_seqs * num_heads * plan.partitions * head_dim;
+    p.ws_ml = p.ws_o + per_layer_o * (lay != nullptr ? lay->layers : 1);
+  }
+  if (lay != nullptr) {
+    p.block_stride = lay->block_stride;
+    p.layer_kv_stride = lay->layer_kv_stride;
+    p.layer_q_stride = (int64_t)num_seqs * num_heads * head_dim;
+    p.layer_ws_stride = (int64_t)num_seqs * num_heads * plan.partitions * head_dim;
+    p.num_layers = lay->layers;
   }
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
@@ -311,6 +332,7 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
     return PA_ERR_INVALID_ARG;
   return from_hip(pa::launch_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
                                        num_blocks, kv_heads, block_size, (int)row_bytes,
+                                       (int64_t)kv_heads * block_size * row_bytes,
                                        (hipStream_t)stream));
 }
 
@@ -469,6 +491,112 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const
   if (r[0] == kPinnedHost && r[2] == kPinnedHost) return PA_ERR_UNSUPPORTED;
   return from_hip(pa::launch_move_blocks((void*)kp[0], (void*)kp[1], dst_num_blocks, kp[2], kp[3],
                                          src_num_blocks, (const int64_t*)kp[4], num_pairs,
+                                         block_bytes, (hipStream_t)stream));
+}
+
+// ---- layered pool: [num_blocks][2][num_layers][kv_heads][block_size][head_dim] ----
+
+static bool layered_args_ok(int32_t num_layers, int32_t kv_heads, int32_t block_size,
+                            int32_t head_dim) {
+  return num_layers > 0 && kv_heads > 0 && block_size > 0 && head_dim > 0;
+}
+
+pa_status pa_kv_append_layered(const void* k_new, const void* v_new, void* kv_pool, int32_t layer,
+                               int32_t num_layers, const int64_t* slot_mapping,
+                               int32_t num_tokens, int32_t num_blocks, int32_t kv_heads,
+                               int32_t block_size, int32_t head_dim, int32_t dtype,
+                               void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || !layered_args_ok(num_layers, kv_heads, block_size,
+                                                             head_dim) ||
+      layer < 0 || layer >= num_layers || !dtype_ok(dtype))
+    return PA_ERR_INVALID_ARG;
+  const int64_t row_bytes = (int64_t)head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !kv_pool || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv_pool, 16) ||
+      !aligned(slot_mapping, 8))
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)num_tokens * 2 * kv_heads * (row_bytes / 16) > (int64_t)INT32_MAX * 256)
+    return PA_ERR_INVALID_ARG;
+  const int64_t layer_bytes = (int64_t)kv_heads * block_size * row_bytes;
+  char* base = (char*)kv_pool;
+  return from_hip(pa::launch_kv_append(k_new, v_new, base + layer * layer_bytes,
+                                       base + ((int64_t)num_layers + layer) * layer_bytes,
+                                       slot_mapping, num_tokens, num_blocks, kv_heads, block_size,
+                                       (int)row_bytes, 2 * num_layers * layer_bytes,
+                                       (hipStream_t)stream));
+}
+
+pa_status pa_decode_layered(void* out, const void* q, const void* kv_pool, int32_t first_layer,
+                            int32_t layers, int32_t num_layers, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            int32_t max_seq_len, int32_t num_seqs, int32_t num_heads,
+                            int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float scale, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, int32_t dtype,
+                            void* stream) {
+  if (!layered_args_ok(num_layers, kv_heads, block_size, head_dim) || layers <= 0 ||
+      first_layer < 0 || first_layer + (int64_t)layers > num_layers || layers > 65535)
+    return PA_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return PA_ERR_INVALID_ARG;
+  const int64_t layer_elems = (int64_t)kv_heads * block_size * head_dim;
+  const char* base = (const char*)kv_pool;
+  const int64_t eb = elem_bytes(dtype);
+  LayerSpec lay;
+  lay.block_stride = 2 * num_layers * layer_elems;
+  lay.layer_kv_stride = layer_elems;
+  lay.layers = layers;
+  const void* k = kv_pool ? base + first_layer * layer_elems * eb : nullptr;
+  const void* v = kv_pool ? base + ((int64_t)num_layers + first_layer) * layer_elems * eb : nullptr;
+  return decode_impl(out, q, k, v, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
+                     num_seqs, num_heads, kv_heads, head_dim, block_size, num_blocks, scale,
+                     partition_size, workspace, workspace_bytes, dtype, PA_KERNEL_MFMA, stream,
+                     nullptr, nullptr, nullptr, &lay);
+}
+
+pa_status pa_copy_blocks_layered(void* kv_pool, const int64_t* block_mapping, int32_t num_pairs,
+                                 int32_t num_blocks, int32_t num_layers, int32_t kv_heads,
+                                 int32_t block_size, int32_t head_dim, int32_t dtype,
+                                 void* stream) {
+  if (num_pairs < 0 || num_blocks <= 0 ||
+      !layered_args_ok(num_layers, kv_heads, block_size, head_dim) || !dtype_ok(dtype))
+    return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes =
+      2 * (int64_t)num_layers * kv_heads * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!kv_pool || !block_mapping || !aligned(kv_pool, 16) || !aligned(block_mapping, 8))
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)num_pairs * 64 > INT32_MAX) return PA_ERR_INVALID_ARG;
+  return from_hip(pa::launch_move_blocks(kv_pool, nullptr, num_blocks, kv_pool, nullptr,
+                                         num_blocks, block_mapping, num_pairs, block_bytes,
+                                         (hipStream_t)stream));
+}
+
+pa_status pa_swap_blocks_layered(void* dst_pool, int64_t dst_num_blocks, const void* src_pool,
+                                 int64_t src_num_blocks, const int64_t* block_mapping,
+                                 int32_t num_pairs, int32_t num_layers, int32_t kv_heads,
+                                 int32_t block_size, int32_t head_dim, int32_t dtype,
+                                 void* stream) {
+  if (num_pairs < 0 || dst_num_blocks <= 0 || src_num_blocks <= 0 ||
+      !layered_args_ok(num_layers, kv_heads, block_size, head_dim) || !dtype_ok(dtype))
+    return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes =
+      2 * (int64_t)num_layers * kv_heads * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if ((int64_t)num_pairs * 64 > INT32_MAX) return PA_ERR_INVALID_ARG;
+  const void* p[3] = {dst_pool, src_pool, block_mapping};
+  const void* kp[3];
+  Residency r[3];
+  for (int i = 0; i < 3; ++i) {
+    r[i] = residency(p[i], &kp[i]);
+    if (r[i] == kUnknown || !aligned(kp[i], i == 2 ? 8 : 16)) return PA_ERR_INVALID_ARG;
+  }
+  if (r[0] == kPinnedHost && r[1] == kPinnedHost) return PA_ERR_UNSUPPORTED;
+  return from_hip(pa::launch_move_blocks((void*)kp[0], nullptr, dst_num_blocks, kp[1], nullptr,
+                                         src_num_blocks, (const int64_t*)kp[2], num_pairs,
                                          block_bytes, (hipStream_t)stream));
 }
 

@@ -38,6 +38,16 @@ struct DecodeParams {
   int32_t partition_size;       // tokens per partition
   int32_t num_partitions;       // grid extent along partitions
   float scale_log2;             // scale * log2(e): scores kept in base-2 units
+  // Layered pool (decode over [NB][2][L][Hkv][BS][D]): k_cache / v_cache point
+  // at the first decoded layer's K / V, blocks lie block_stride elements
+  // apart, and launch layer y = blockIdx.y adds y * layer_kv_stride to both
+  // caches, y * layer_q_stride to q and out and y * layer_ws_stride to ws_o
+  // (y * layer_ws_stride / D * 2 to ws_ml).  Unused (0) for one per-layer pool.
+  int64_t block_stride;
+  int64_t layer_kv_stride;
+  int64_t layer_q_stride;
+  int64_t layer_ws_stride;
+  int32_t num_layers;           // grid extent along layers (1 without layering)
 };
 
 // Everything a chunked-prefill launch needs.
@@ -162,8 +172,11 @@ __device__ inline uint16_t f32_to_bf16(float f) {
 // ---- launchers (return the launch status) --------------------------------
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int64_t* slots, int num_tokens, int64_t num_blocks,
-                            int kv_heads, int block_size, int row_bytes, hipStream_t stream);
+                            int kv_heads, int block_size, int row_bytes, int64_t block_bytes,
+                            hipStream_t stream);
 
+// dst_v == nullptr: one-part pools (the layered layout, whole blocks of
+// block_bytes); otherwise K and V pools with block_bytes per part.
 hipError_t launch_move_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, const void* src_k,
                               const void* src_v, int64_t src_blocks, const int64_t* pairs,
                               int num_pairs, int64_t block_bytes, hipStream_t stream);

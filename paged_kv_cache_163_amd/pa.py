@@ -14,6 +14,8 @@ Tensor layouts (C-contiguous):
     k_new, v_new        [num_tokens, kv_heads, head_dim]
     slot_mapping        int64 [num_tokens]
     block_mapping       int64 [num_pairs, 2]   (src, dst)
+    kv_pool (layered)   [num_blocks, 2, num_layers, kv_heads, block_size, head_dim]
+    layered q, out      [layers, num_seqs, num_heads, head_dim]
     prefill q, out      [num_queries, num_heads, head_dim]       bfloat16
     query_start         int32 [num_seqs + 1]   chunk offsets into the prefill q
 """
@@ -81,6 +83,14 @@ _bm_decode_inputs = _sig("pa_bm_decode_inputs", _i32, _vp, _P(_i64), _i32, _i32,
 _bm_sequence = _sig("pa_bm_sequence", _i32, _vp, _i64, _P(_i64), _P(_i64), _P(_i32))
 _bm_stats = _sig("pa_bm_stats", _i32, _vp, _P(_i64), _P(_i64), _P(_i64))
 _bm_refcount = _sig("pa_bm_refcount", _i32, _vp, _i64, _i32, _P(_i32))
+_kv_append_layered = _sig("pa_kv_append_layered", _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _i32,
+                          _i32, _i32, _i32, _i32, _vp)
+_decode_layered = _sig("pa_decode_layered", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp,
+                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp)
+_copy_blocks_layered = _sig("pa_copy_blocks_layered", _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                            _i32, _i32, _vp)
+_swap_blocks_layered = _sig("pa_swap_blocks_layered", _i32, _vp, _i64, _vp, _i64, _vp, _i32, _i32,
+                            _i32, _i32, _i32, _i32, _vp)
 _swap_blocks = _sig("pa_swap_blocks", _i32, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                     _i32, _i32, _vp)
 _prefill = _sig("pa_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -91,7 +101,9 @@ EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_appe
             "pa_decode_append", "pa_copy_blocks", "pa_prefill", "pa_swap_blocks",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_can_admit", "pa_bm_admit", "pa_bm_fork",
             "pa_bm_append_slots", "pa_bm_release", "pa_bm_swap_out", "pa_bm_swap_in",
-            "pa_bm_decode_inputs", "pa_bm_sequence", "pa_bm_stats", "pa_bm_refcount"]
+            "pa_bm_decode_inputs", "pa_bm_sequence", "pa_bm_stats", "pa_bm_refcount",
+            "pa_kv_append_layered", "pa_decode_layered", "pa_copy_blocks_layered",
+            "pa_swap_blocks_layered"]
 
 
 def abi_version() -> int:
@@ -446,3 +458,83 @@ class BlockManager:
         r = _i32()
         _check(_bm_refcount(self._h, int(block), int(host), ctypes.byref(r)), "bm_refcount")
         return r.value
+
+
+# ---- layered pool: [num_blocks, 2, num_layers, kv_heads, block_size, head_dim] ----
+
+def _pool_dims(kv_pool):
+    if kv_pool.dim() != 6 or kv_pool.shape[1] != 2:
+        raise ValueError("kv_pool must be [num_blocks, 2, num_layers, kv_heads, block_size, head_dim]")
+    nb, _, nl, hkv, bs, d = kv_pool.shape
+    return nb, nl, hkv, bs, d
+
+
+def kv_append_layered(k_new, v_new, kv_pool, layer, slot_mapping, stream=None) -> None:
+    """Append layer ``layer``'s new rows ([num_tokens, kv_heads, head_dim]) into a layered pool."""
+    nb, nl, hkv, bs, d = _pool_dims(kv_pool)
+    if k_new.shape != v_new.shape or k_new.dim() != 3 or k_new.shape[1:] != (hkv, d):
+        raise ValueError("k_new/v_new must be [num_tokens, kv_heads, head_dim]")
+    if k_new.dtype != kv_pool.dtype or v_new.dtype != kv_pool.dtype:
+        raise ValueError("dtype mismatch")
+    if slot_mapping.dim() != 1 or slot_mapping.shape[0] != k_new.shape[0]:
+        raise ValueError("slot_mapping must be [num_tokens]")
+    _check(_kv_append_layered(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(kv_pool, "kv_pool"),
+                              int(layer), nl, _dev(slot_mapping, "slot_mapping", torch.int64),
+                              k_new.shape[0], nb, hkv, bs, d, _dtype_code(kv_pool), _stream(stream)),
+           "kv_append_layered")
+
+
+def decode_layered(q, kv_pool, block_tables, seq_lens, scale, first_layer=0, max_seq_len=None,
+                   partition_size=0, out=None, workspace=None, stream=None):
+    """Decode q [layers, num_seqs, num_heads, head_dim] over layers
+    first_layer .. first_layer + layers - 1 of a layered pool, in one launch."""
+    nb, nl, hkv, bs, d = _pool_dims(kv_pool)
+    if q.dim() != 4 or q.shape[3] != d:
+        raise ValueError("q must be [layers, num_seqs, num_heads, head_dim]")
+    L, B, hq, _ = q.shape
+    if q.dtype != kv_pool.dtype:
+        raise ValueError("q and kv_pool must share a dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_tables [num_seqs, max_blocks], seq_lens [num_seqs]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
+    ws = decode_plan(B, hq, hkv, d, bs, max_seq_len, partition_size, q.dtype, "mfma").workspace_bytes * L
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if ws > 0 and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_decode_layered(_dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+                           int(first_layer), L, nl, _dev(block_tables, "block_tables", torch.int32),
+                           block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
+                           int(max_seq_len), B, hq, hkv, d, bs, nb, float(scale),
+                           int(partition_size), ws_ptr, ws_len, _dtype_code(q), _stream(stream)),
+           "decode_layered")
+    return out
+
+
+def copy_blocks_layered(kv_pool, block_mapping, stream=None) -> None:
+    nb, nl, hkv, bs, d = _pool_dims(kv_pool)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    _check(_copy_blocks_layered(_dev(kv_pool, "kv_pool"),
+                                _dev(block_mapping, "block_mapping", torch.int64),
+                                block_mapping.shape[0], nb, nl, hkv, bs, d, _dtype_code(kv_pool),
+                                _stream(stream)), "copy_blocks_layered")
+
+
+def swap_blocks_layered(dst_pool, src_pool, block_mapping, stream=None) -> None:
+    """Whole layered blocks between a device pool and a pinned host pool (either way)."""
+    dnb, nl, hkv, bs, d = _pool_dims(dst_pool)
+    snb, nl2, hkv2, bs2, d2 = _pool_dims(src_pool)
+    if (nl, hkv, bs, d) != (nl2, hkv2, bs2, d2) or dst_pool.dtype != src_pool.dtype:
+        raise ValueError("pools must share the block shape and dtype")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2]")
+    _check(_swap_blocks_layered(_ptr_any(dst_pool, "dst_pool"), dnb, _ptr_any(src_pool, "src_pool"),
+                                snb, _ptr_any(block_mapping, "block_mapping", torch.int64),
+                                block_mapping.shape[0], nl, hkv, bs, d, _dtype_code(src_pool),
+                                _stream(stream)), "swap_blocks_layered")

@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--workload", default="llama70b",
                     help="llama70b | shared_prefix | long_context | sweep_b{16,32,64}_d{64,128} "
                          "| prefill_llama70b | prefill_chunked (one pa_prefill launch per step) "
-                         "| swap_llama70b (block swap to pinned host memory and back)")
+                         "| swap_llama70b (block swap to pinned host memory and back) "
+                         "| layered_llama70b (8 layers of a layered pool per launch)")
     ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled over steps")
     ap.add_argument("--partition", type=int, default=0, help="0 = library's choice")
     ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "valu"])
@@ -361,6 +362,82 @@ def swap_main(args, np, torch, W, pa, dev):
     print(json.dumps(line), flush=True)
 
 
+def layered_main(args, np, torch, W, pa, dev, layers=8):
+    """The 70B-shaped decode batch over a layered pool of `layers` layers
+    ([num_blocks, 2, layers, 8, 16, 128] bf16, filled on the device): all
+    layers in one pa_decode_layered launch, against one launch per layer."""
+    w = W.llama70b(append=False)
+    shape = (w.num_blocks, 2, layers, w.kv_heads, w.block_size, w.head_dim)
+    pool = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev).manual_seed(0)
+    pool.normal_(generator=g)
+    q = torch.empty((layers,) + w.q.shape, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    out = torch.empty_like(q)
+    plan = pa.decode_plan(w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size,
+                          w.max_seq_len, 0, torch.bfloat16, "mfma")
+    ws = torch.empty(max(plan.workspace_bytes * layers, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def all_layers():
+        pa.decode_layered(q, pool, bt, lens, w.scale, max_seq_len=w.max_seq_len, out=out,
+                          workspace=ws)
+
+    def per_layer():
+        for layer in range(layers):
+            pa.decode_layered(q[layer:layer + 1], pool, bt, lens, w.scale, first_layer=layer,
+                              max_seq_len=w.max_seq_len, out=out[layer:layer + 1], workspace=ws)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        timer = HipTimer()
+        a, b = timer.event(), timer.event()
+        timer.record(a, stream)
+        for _ in range(args.steps):
+            fn()
+        timer.record(b, stream)
+        torch.cuda.synchronize()
+        ms = timer.elapsed_ms(a, b) / args.steps
+        timer.close()
+        return ms
+
+    one_ms = timed(all_layers)
+    each_ms = timed(per_layer)
+    kv_bytes = layers * W.decode_kv_bytes(w.seq_lens, w.kv_heads, w.head_dim, w.elem_bytes)
+    gbs = kv_bytes / (one_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC + " (layered pool, all layers per launch)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(one_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "layered_llama70b", "layers": layers, "num_seqs": w.num_seqs,
+                   "num_heads": w.num_heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "partition_size": plan.partition_size, "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "one_launch_per_layer": {"ms": round(each_ms, 5),
+                                 "GBps": round(kv_bytes / (each_ms * 1e-3) / 1e9, 2)},
+        "kv_bytes_per_step": kv_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_mfma_kernel (layered)", "bytes_per_launch": kv_bytes,
+                     "avg_launch_ms": round(one_ms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -385,6 +462,8 @@ def main():
         return prefill_main(args, np, torch, W, pa, dev)
     if args.workload == "swap_llama70b":
         return swap_main(args, np, torch, W, pa, dev)
+    if args.workload == "layered_llama70b":
+        return layered_main(args, np, torch, W, pa, dev)
 
     if args.copy_calibration:
         n = 1 << 30

@@ -425,3 +425,26 @@ def test_fused_append_decode_full_size(pa):
     with pytest.raises(NotImplementedError):
         pa.decode_append(d["q"], d["k"], d["v"], dev(k), dev(v), dev(slots), d["bt"], d["lens"],
                          w.scale, max_seq_len=w.max_seq_len, kernel="stream")
+
+
+@pytest.mark.parametrize("batch", [600, 4500])
+def test_longest_first_ranking_large_batches(pa, batch):
+    """Batches past the ranking's in-register lengths (> 512 sequences: lengths
+    re-read from memory) and past its size limit (> 4096: index order), with
+    lengths in few bins and many ties; every sequence must get its own output."""
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(1, 80, size=batch).tolist()
+    lens[::97] = [0] * len(lens[::97])            # empty sequences scattered through the batch
+    w = small_bf16(lens, 16, 64, 8, 2, seed=batch)
+    d = upload(w)
+    out = decode(pa, d, w, kernel="mfma")
+    got = as_f64(out)
+    seqs = sample_seqs(w, 64, seed=batch) + [0, batch - 1]
+    seqs = sorted(set(seqs))
+    assert_close(got[seqs], oracle_decode(w, seqs=seqs), "bf16", f"B={batch}")
+    empty = [s for s in range(batch) if lens[s] == 0]
+    assert np.all(got[empty] == 0.0)
+    # all outputs are distinct rows (no two sequences mapped to one work item)
+    rows = got[:, 0, :4]
+    live = [s for s in range(batch) if lens[s] > 0]
+    assert len({tuple(r) for r in rows[live]}) == len(live)

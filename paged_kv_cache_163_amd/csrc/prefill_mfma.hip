@@ -10,16 +10,18 @@
 //
 // Rows are (chunk query, query head) pairs of one KV head's GQA group: row r
 // of a work-group is query i0 + r / G, head g = r % G, so the G heads that
-// share a KV head share every K/V load.  A work-group of 4 waves covers
-// kPrefillRows rows; each wave owns 64 of them as four 16-row column tiles
-// of the MFMA step from mfma_step.h (S^T = K Q^T, O^T += V^T P^T; its Q rows
-// wait in LDS, read back as the B operands of every step), and walks
-// the keys [0, last position of its rows] in 32-token steps, loading each
-// step once for its four tiles and one step ahead of the math.  The causal
-// limit is per lane (a lane's score column is one row); V rows past the
-// wave's last key are zeroed so tail slots never reach the sum.  The first
-// step holds key 0, which every row sees, so no row's running max stays
-// -inf after it.
+// share a KV head share every K/V load.  A work-group of kPfWaves waves covers
+// kPrefillRows rows; each wave owns kRowTiles 16-row column tiles of the MFMA
+// step from mfma_step.h (S^T = K Q^T, O^T += V^T P^T) with its Q^T operands in
+// registers.  The work-group walks the keys [0, last position of its rows]
+// in 32-token steps: every thread loads 16-byte parts of the next step's K
+// and V tiles from HBM while the waves compute the current one from LDS
+// (double-buffered, one barrier per step), so each K/V byte is fetched once
+// per work-group.  A wave whose rows end earlier skips the math of the later
+// steps.  The causal limit is per lane (a lane's score column is one row); V
+// rows past the wave's last key are zeroed so tail slots never reach the
+// sum.  The first step holds key 0, which every row sees, so no row's
+// running max stays -inf after it.
 //
 // Work order: work-group x runs on XCD x % 8.  All query tiles of one
 // (sequence, KV head) pair are given consecutive slots on one XCD, latest
@@ -32,15 +34,22 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kPfWaves = 4;
-constexpr int kRowTiles = 3;                 // 16-row MFMA column tiles per wave
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = kPfWaves * 64;
+constexpr int kRowTiles = 2;                 // 16-row MFMA column tiles per wave
 constexpr int kWaveRows = 16 * kRowTiles;
 static_assert(kPfWaves * kWaveRows == kPrefillRows, "work-group rows");
-// LDS bytes per staged Q row: 16 bytes of padding move consecutive rows to
-// other banks, so the 16 lanes that read one 16-byte column of 16 rows do
+// LDS bytes per staged K or V row: 16 bytes of padding move consecutive rows
+// to other banks, so the 16 lanes that read one 16-byte column of 16 rows do
 // not collide.
 template <int D>
-constexpr int kQStride = D * 2 + 16;
+constexpr int kKvStride = D * 2 + 16;
+template <int D>
+constexpr int kRowParts = D * 2 / 16;        // 16-byte parts of a K or V row
+template <int D>
+constexpr int kStageParts = 2 * 32 * kRowParts<D> / kPfThreads;  // per thread per step
+static_assert(2 * 32 * kRowParts<128> % kPfThreads == 0 && 2 * 32 * kRowParts<64> % kPfThreads == 0,
+              "every thread stages whole parts");
 
 // A row's running state: O^T tiles, the row sum (computed on the matrix core
 // as P^T against a ones operand, so it is the exact sum of the bf16 P the
@@ -77,12 +86,11 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {  // round to nearest 
 
 // One 32-key step for all row tiles of a wave.  With kMask, keys > lim[nr]
 // (the lane's row position) are masked; V rows at or past kend are zeroed.
-// Q^T operands come from the wave's rows staged in LDS (qlds: this lane's
-// row of tile 0, kQStride bytes per row).  c = scale * log2(e) > 0 (the host
-// rejects other scales), so the row max of c*s is c times the max of s.
+// c = scale * log2(e) > 0 (the host rejects other scales), so the row max of
+// c*s is c times the max of s.
 template <int D, bool kMask>
 __device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
-                                    const unsigned char* qlds, int base, int kend,
+                                    const u32x4 (&qb)[kRowTiles][D / 32], int base, int kend,
                                     const int (&lim)[kRowTiles], float c, int q4) {
   constexpr int kKi = D / 32;
   constexpr int kVd = D / 16;
@@ -113,8 +121,7 @@ __device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
     for (int kt = 0; kt < 2; ++kt) {
       s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < kKi; ++i)
-        s[kt] = mma(r.k[kt][i], *(const u32x4*)(qlds + nr * 16 * kQStride<D> + 64 * i), s[kt]);
+      for (int i = 0; i < kKi; ++i) s[kt] = mma(r.k[kt][i], qb[nr][i], s[kt]);
     }
     float sv[8];
     float mr = -INFINITY;
@@ -145,6 +152,73 @@ __device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
     a[nr].l = mma(ones, pb, a[nr].l);
 #pragma unroll
     for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt]);
+  }
+}
+
+// The K and V tiles of one 32-key step, staged by the whole work-group:
+// thread t holds parts t, t + kPfThreads, ... of the step's 2*32 rows (K rows
+// first), 16 bytes each.  Keys past the sequence re-read its last live block
+// (masked later); a table entry outside the pool sets `bad` (work-group
+// uniform) and reads block 0 instead.
+template <int D>
+struct Stage {
+  u32x4 part[kStageParts<D>];
+};
+
+template <int D>
+__device__ inline void stage_load(Stage<D>& st, const SeqView& c, int base, int tid, bool& bad) {
+  int phys[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int lb = min((base + 16 * kt) >> c.block_shift, c.nblocks_valid - 1);
+    phys[kt] = c.table[lb];
+    if (phys[kt] < 0 || phys[kt] >= c.num_blocks) {
+      bad = true;
+      phys[kt] = 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kStageParts<D>; ++j) {
+    const int idx = tid + kPfThreads * j;
+    const int kv = idx / (32 * kRowParts<D>);
+    const int rem = idx - kv * 32 * kRowParts<D>;
+    const int row = rem / kRowParts<D>;
+    const int col = rem - row * kRowParts<D>;
+    const int kt = row >> 4;
+    const int64_t off = (int64_t)phys[kt] * c.block_stride +
+                        (int64_t)(((base + 16 * kt) & c.bmask) + (row & 15)) * (D * 2) + col * 16;
+    st.part[j] = *(const u32x4*)((kv ? c.vbase : c.kbase) + off);
+  }
+}
+
+template <int D>
+__device__ inline void stage_store(const Stage<D>& st, unsigned char* buf, int tid) {
+#pragma unroll
+  for (int j = 0; j < kStageParts<D>; ++j) {
+    const int idx = tid + kPfThreads * j;
+    const int kv = idx / (32 * kRowParts<D>);
+    const int rem = idx - kv * 32 * kRowParts<D>;
+    const int row = rem / kRowParts<D>;
+    const int col = rem - row * kRowParts<D>;
+    *(u32x4*)(buf + (kv * 32 + row) * kKvStride<D> + col * 16) = st.part[j];
+  }
+}
+
+// A wave's MFMA operands of one step from the staged tiles (the layout the
+// register loads of mfma_step.h produce).
+template <int D>
+__device__ inline void read_step(StepRegs<D>& r, const unsigned char* buf, int r16, int q4) {
+  const unsigned char* ks = buf;
+  const unsigned char* vs = buf + 32 * kKvStride<D>;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+      r.k[kt][i] = *(const u32x4*)(ks + (16 * kt + r16) * kKvStride<D> + 64 * i + 16 * q4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int tok = 16 * (e >> 2) + 4 * q4 + (e & 3);
+    r.v[e] = *(const typename VRow<D>::T*)(vs + tok * kKvStride<D> + r16 * (D / 16) * 2);
   }
 }
 
@@ -202,40 +276,31 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillPara
     return;
   }
   const int i0 = tile * (kPrefillRows / G);  // first chunk query of the work-group
+  if (i0 >= nq) return;                       // the whole work-group: past the chunk
+  const int pos0 = len - nq;                  // position of chunk query 0
+  const int kend_wg = pos0 + min(nq - 1, i0 + (kPrefillRows - 1) / G) + 1;
   const int wrow0 = wave * kWaveRows;
   const int wi_first = i0 + wrow0 / G;
-  if (wi_first >= nq) return;  // this wave has no rows (the kernel has no barrier)
-  const int wi_last = min(nq - 1, i0 + (wrow0 + kWaveRows - 1) / G);
-  const int pos0 = len - nq;   // position of chunk query 0
-  const int kend = pos0 + wi_last + 1;
+  const bool wave_rows = wi_first < nq;       // a wave past the chunk still stages tiles
+  const int kend = wave_rows ? pos0 + min(nq - 1, i0 + (wrow0 + kWaveRows - 1) / G) + 1 : 0;
 
-  // The wave stages its 64 Q rows in LDS (zero rows past the chunk); each
-  // lane keeps the causal limit of its row in every tile.
-  __shared__ __attribute__((aligned(16))) unsigned char sm_q[kPfWaves][kWaveRows * kQStride<D>];
-  unsigned char* wq = sm_q[wave];
-  {
-    constexpr int kParts = D * 2 / 16;  // 16-byte parts per row
-    for (int k = lane; k < kWaveRows * kParts; k += 64) {
-      const int rw = k / kParts;
-      const int part = k - rw * kParts;
-      const int row = wrow0 + rw;
-      const int qi = i0 + row / G;
-      const int g = row - (row / G) * G;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (qi < nq)
-        v = *(const u32x4*)((const char*)p.q +
-                            ((int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D) * 2 + part * 16);
-      *(u32x4*)(wq + rw * kQStride<D> + part * 16) = v;
-    }
-  }
+  // Q^T operands of the lane's row in each tile (zero past the chunk) and the
+  // causal limit of that row.
+  u32x4 qb[kRowTiles][D / 32];
   int lim[kRowTiles];
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr) {
-    const int qi = i0 + (wrow0 + 16 * nr + r16) / G;
-    lim[nr] = qi < nq ? pos0 + qi : 0;
+    const int row = wrow0 + 16 * nr + r16;
+    const int qi = i0 + row / G;
+    const int g = row - (row / G) * G;
+    const bool valid = qi < nq;
+    lim[nr] = valid ? pos0 + qi : 0;
+    const char* qrow =
+        (const char*)p.q + ((int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D) * 2 + q4 * 16;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+      qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
   }
-  __builtin_amdgcn_wave_barrier();  // one wave's LDS writes and reads stay in order
-  const unsigned char* qlds = wq + r16 * kQStride<D> + q4 * 16;
 
   SeqView c;
   const int64_t head_stride = (int64_t)p.block_size * D * 2;
@@ -258,23 +323,27 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillPara
   }
   bool bad = false;
 
-  int base = 0;
+  __shared__ __attribute__((aligned(16))) unsigned char sm_kv[2][2 * 32 * kKvStride<D>];
   {
-    StepRegs<D> ra, rb;
-    load_step<D, false>(ra, c, base, r16, q4, bad);
-    while (true) {
-      int next = base + 32;
-      if (next < kend) load_step<D, false>(rb, c, next, r16, q4, bad);
-      prefill_step<D, true>(ra, a, qlds, base, kend, lim, p.scale_log2, q4);
-      base = next;
-      if (base >= kend) break;
-      next = base + 32;
-      if (next < kend) load_step<D, false>(ra, c, next, r16, q4, bad);
-      prefill_step<D, true>(rb, a, qlds, base, kend, lim, p.scale_log2, q4);
-      base = next;
-      if (base >= kend) break;
+    Stage<D> st;
+    stage_load<D>(st, c, 0, tid, bad);
+    stage_store<D>(st, sm_kv[0], tid);
+    __syncthreads();
+    int buf = 0;
+    for (int base = 0; base < kend_wg; base += 32) {
+      const bool more = base + 32 < kend_wg;
+      if (more) stage_load<D>(st, c, base + 32, tid, bad);  // in flight during the math
+      if (base < kend) {
+        StepRegs<D> r;
+        read_step<D>(r, sm_kv[buf], r16, q4);
+        prefill_step<D, true>(r, a, qb, base, kend, lim, p.scale_log2, q4);
+      }
+      if (more) stage_store<D>(st, sm_kv[buf ^ 1], tid);
+      __syncthreads();
+      buf ^= 1;
     }
   }
+  if (!wave_rows) return;
 
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr) {

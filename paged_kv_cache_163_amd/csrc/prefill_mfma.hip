@@ -85,13 +85,15 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {  // round to nearest 
 }
 
 // One 32-key step for all row tiles of a wave.  With kMask, keys > lim[nr]
-// (the lane's row position) are masked; V rows at or past kend are zeroed.
+// (the lane's row position) are masked, unless the whole step lies at or
+// before kfull, the wave's first row position; V rows at or past kend are
+// zeroed.
 // c = scale * log2(e) > 0 (the host rejects other scales), so the row max of
 // c*s is c times the max of s.
 template <int D, bool kMask>
 __device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
                                     const u32x4 (&qb)[kRowTiles][D / 32], int base, int kend,
-                                    const int (&lim)[kRowTiles], float c, int q4) {
+                                    int kfull, const int (&lim)[kRowTiles], float c, int q4) {
   constexpr int kKi = D / 32;
   constexpr int kVd = D / 16;
   if (base + 32 > kend) {
@@ -124,16 +126,18 @@ __device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
       for (int i = 0; i < kKi; ++i) s[kt] = mma(r.k[kt][i], qb[nr][i], s[kt]);
     }
     float sv[8];
-    float mr = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sv[e] = s[e >> 2][e & 3];
-      if constexpr (kMask) {
+    for (int e = 0; e < 8; ++e) sv[e] = s[e >> 2][e & 3];
+    if (kMask && base + 31 > kfull) {  // wave-uniform: some row does not see the whole step
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
         const int tok = base + 16 * (e >> 2) + 4 * q4 + (e & 3);
         sv[e] = tok <= lim[nr] ? sv[e] : -INFINITY;
       }
-      mr = fmaxf(mr, sv[e]);
     }
+    float mr = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mr = fmaxf(mr, sv[e]);
     const float mx = row_max4(mr) * c;
     if (__builtin_amdgcn_ballot_w64(mx > a[nr].m + kSlack) != 0) {  // wave-uniform
       const float m_new = fmaxf(a[nr].m, mx);
@@ -283,6 +287,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillPara
   const int wi_first = i0 + wrow0 / G;
   const bool wave_rows = wi_first < nq;       // a wave past the chunk still stages tiles
   const int kend = wave_rows ? pos0 + min(nq - 1, i0 + (wrow0 + kWaveRows - 1) / G) + 1 : 0;
+  // Last key every row of the wave sees (rows past the chunk have zero
+  // queries and are never written, so unmasked steps may show them any key
+  // below kend).
+  const int kfull = pos0 + wi_first;
 
   // Q^T operands of the lane's row in each tile (zero past the chunk) and the
   // causal limit of that row.
@@ -336,7 +344,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillPara
       if (base < kend) {
         StepRegs<D> r;
         read_step<D>(r, sm_kv[buf], r16, q4);
-        prefill_step<D, true>(r, a, qb, base, kend, lim, p.scale_log2, q4);
+        prefill_step<D, true>(r, a, qb, base, kend, kfull, lim, p.scale_log2, q4);
       }
       if (more) stage_store<D>(st, sm_kv[buf ^ 1], tid);
       __syncthreads();

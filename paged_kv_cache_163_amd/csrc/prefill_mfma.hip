@@ -161,26 +161,27 @@ __device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
 
 // The K and V tiles of one 32-key step, staged by the whole work-group:
 // thread t holds parts t, t + kPfThreads, ... of the step's 2*32 rows (K rows
-// first), 16 bytes each.  Keys past the sequence re-read its last live block
-// (masked later); a table entry outside the pool sets `bad` (work-group
-// uniform) and reads block 0 instead.
+// first), 16 bytes each.  A part keeps its row, column and K|V role from step
+// to step, so its byte offsets inside the block tile and inside the LDS tile
+// are fixed per thread (StagePlan); a step only adds the two 16-token tiles'
+// block offsets.  Keys past the sequence re-read its last live block (masked
+// later); a table entry outside the pool sets `bad` (work-group uniform) and
+// reads block 0 instead.
 template <int D>
 struct Stage {
   u32x4 part[kStageParts<D>];
 };
 
 template <int D>
-__device__ inline void stage_load(Stage<D>& st, const SeqView& c, int base, int tid, bool& bad) {
-  int phys[2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int lb = min((base + 16 * kt) >> c.block_shift, c.nblocks_valid - 1);
-    phys[kt] = c.table[lb];
-    if (phys[kt] < 0 || phys[kt] >= c.num_blocks) {
-      bad = true;
-      phys[kt] = 0;
-    }
-  }
+struct StagePlan {
+  const char* src[kStageParts<D>];   // K or V base + row-in-tile and column offset
+  uint32_t lds[kStageParts<D>];      // byte offset in an LDS tile
+  bool hi[kStageParts<D>];           // the part's row is in the step's second 16-token tile
+};
+
+template <int D>
+__device__ inline StagePlan<D> stage_plan(const SeqView& c, int tid) {
+  StagePlan<D> sp;
 #pragma unroll
   for (int j = 0; j < kStageParts<D>; ++j) {
     const int idx = tid + kPfThreads * j;
@@ -188,24 +189,37 @@ __device__ inline void stage_load(Stage<D>& st, const SeqView& c, int base, int 
     const int rem = idx - kv * 32 * kRowParts<D>;
     const int row = rem / kRowParts<D>;
     const int col = rem - row * kRowParts<D>;
-    const int kt = row >> 4;
-    const int64_t off = (int64_t)phys[kt] * c.block_stride +
-                        (int64_t)(((base + 16 * kt) & c.bmask) + (row & 15)) * (D * 2) + col * 16;
-    st.part[j] = *(const u32x4*)((kv ? c.vbase : c.kbase) + off);
+    sp.src[j] = (kv ? c.vbase : c.kbase) + (row & 15) * (D * 2) + col * 16;
+    sp.lds[j] = (uint32_t)((kv * 32 + row) * kKvStride<D> + col * 16);
+    sp.hi[j] = row >= 16;
   }
+  return sp;
 }
 
 template <int D>
-__device__ inline void stage_store(const Stage<D>& st, unsigned char* buf, int tid) {
+__device__ inline void stage_load(Stage<D>& st, const StagePlan<D>& sp, const SeqView& c,
+                                  int base, bool& bad) {
+  int64_t tile[2];
 #pragma unroll
-  for (int j = 0; j < kStageParts<D>; ++j) {
-    const int idx = tid + kPfThreads * j;
-    const int kv = idx / (32 * kRowParts<D>);
-    const int rem = idx - kv * 32 * kRowParts<D>;
-    const int row = rem / kRowParts<D>;
-    const int col = rem - row * kRowParts<D>;
-    *(u32x4*)(buf + (kv * 32 + row) * kKvStride<D> + col * 16) = st.part[j];
+  for (int kt = 0; kt < 2; ++kt) {
+    const int tok0 = base + 16 * kt;
+    const int lb = min(tok0 >> c.block_shift, c.nblocks_valid - 1);
+    int phys = c.table[lb];
+    if (phys < 0 || phys >= c.num_blocks) {
+      bad = true;
+      phys = 0;
+    }
+    tile[kt] = (int64_t)phys * c.block_stride + (int64_t)(tok0 & c.bmask) * (D * 2);
   }
+#pragma unroll
+  for (int j = 0; j < kStageParts<D>; ++j)
+    st.part[j] = *(const u32x4*)(sp.src[j] + (sp.hi[j] ? tile[1] : tile[0]));
+}
+
+template <int D>
+__device__ inline void stage_store(const Stage<D>& st, const StagePlan<D>& sp, unsigned char* buf) {
+#pragma unroll
+  for (int j = 0; j < kStageParts<D>; ++j) *(u32x4*)(buf + sp.lds[j]) = st.part[j];
 }
 
 // A wave's MFMA operands of one step from the staged tiles (the layout the
@@ -333,20 +347,21 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillPara
 
   __shared__ __attribute__((aligned(16))) unsigned char sm_kv[2][2 * 32 * kKvStride<D>];
   {
+    const StagePlan<D> sp = stage_plan<D>(c, tid);
     Stage<D> st;
-    stage_load<D>(st, c, 0, tid, bad);
-    stage_store<D>(st, sm_kv[0], tid);
+    stage_load<D>(st, sp, c, 0, bad);
+    stage_store<D>(st, sp, sm_kv[0]);
     __syncthreads();
     int buf = 0;
     for (int base = 0; base < kend_wg; base += 32) {
       const bool more = base + 32 < kend_wg;
-      if (more) stage_load<D>(st, c, base + 32, tid, bad);  // in flight during the math
+      if (more) stage_load<D>(st, sp, c, base + 32, bad);  // in flight during the math
       if (base < kend) {
         StepRegs<D> r;
         read_step<D>(r, sm_kv[buf], r16, q4);
         prefill_step<D, true>(r, a, qb, base, kend, kfull, lim, p.scale_log2, q4);
       }
-      if (more) stage_store<D>(st, sm_kv[buf ^ 1], tid);
+      if (more) stage_store<D>(st, sp, sm_kv[buf ^ 1]);
       __syncthreads();
       buf ^= 1;
     }

@@ -183,7 +183,7 @@ hipError_t launch_move_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, cons
 
 // is_bf16: element type of q/out/caches; head_dim in {64, 128}; group in {1,2,4,8}.
 // Rows of (position, query head) one prefill work-group covers.
-constexpr int kPrefillRows = 256;
+constexpr int kPrefillRows = 128;
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t stream);
 
 hipError_t launch_decode_valu(const DecodeParams& p, bool is_bf16, int head_dim,

@@ -34,7 +34,7 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kPfWaves = 8;
+constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kRowTiles = 2;                 // 16-row MFMA column tiles per wave
 constexpr int kWaveRows = 16 * kRowTiles;
@@ -255,7 +255,8 @@ __device__ inline void store_row_part(uint16_t* dst, const float* v) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kPfWaves * 64) void prefill_mfma_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_mfma_kernel(PrefillParams p) {
   constexpr int kVd = D / 16;
   const int pairs = p.num_seqs * p.kv_heads;
   const int x = blockIdx.x;

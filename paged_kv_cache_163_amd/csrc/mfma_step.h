@@ -29,6 +29,10 @@
 //    registers with byte permutes.  Row i of output tile jt is head
 //    dimension VD*i + jt.
 //
+// Exponentials are v_exp_f32 (__builtin_amdgcn_exp2f): no denormal results,
+// which only removes probabilities below 2^-126 that bf16 rounding keeps as
+// denormals; measured ~0.6 % faster than the library exp2f on the 70B batch.
+//
 // Softmax per step in base-2 units: step max over the lane's 8 scores and
 // its 3 partner lanes; (m, l, O) rescaled when the max rises; p =
 // exp2(s - m) rounded to bf16 for the PV product and summed into l in that
@@ -172,13 +176,13 @@ __device__ inline void compute_step(StepRegs<D>& r, Acc<D>& a, const u32x4* qb, 
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(a.m, mx);
   const float m_ref = (kMayBeEmpty && m_new == -INFINITY) ? 0.f : m_new;
-  const float keep = exp2f(a.m - m_ref);  // 0 on the first step
+  const float keep = __builtin_amdgcn_exp2f(a.m - m_ref);  // 0 on the first step
   u32x4 pb;
   float psum = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const uint32_t lo = f32_to_bf16(exp2f(t[2 * u] - m_ref));
-    const uint32_t hi = f32_to_bf16(exp2f(t[2 * u + 1] - m_ref));
+    const uint32_t lo = f32_to_bf16(__builtin_amdgcn_exp2f(t[2 * u] - m_ref));
+    const uint32_t hi = f32_to_bf16(__builtin_amdgcn_exp2f(t[2 * u + 1] - m_ref));
     pb[u] = lo | (hi << 16);
     psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
   }
@@ -233,8 +237,8 @@ __device__ inline void add_token(Acc<D>& a, const u32x4* qb, const unsigned char
   part += __shfl_xor(part, 32);
   const float s = part * scale_log2;
   const float m_new = fmaxf(a.m, s);
-  const float keep = exp2f(a.m - m_new);
-  const uint32_t pbits = f32_to_bf16(exp2f(s - m_new));
+  const float keep = __builtin_amdgcn_exp2f(a.m - m_new);
+  const uint32_t pbits = f32_to_bf16(__builtin_amdgcn_exp2f(s - m_new));
   const float pr = __uint_as_float(pbits << 16);
   a.l = a.l * keep + (q4 == 0 ? pr : 0.f);  // one share per r16
   a.m = m_new;

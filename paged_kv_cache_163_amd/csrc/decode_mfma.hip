@@ -132,7 +132,8 @@ __device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_his
 
 // kModePlain: one per-layer pool.  kModeFused: plus the step's append.
 // kModeLayered: one or more layers of a layered pool (layer = blockIdx.y).
-enum Mode { kModePlain, kModeFused, kModeLayered };
+// kModeOrdered: a per-layer pool with the caller's longest-first order.
+enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered };
 
 template <int D, int M>
 __global__ __launch_bounds__(kWaves * 64)
@@ -149,7 +150,15 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ int sm_pick[2];
   __shared__ __attribute__((aligned(16))) unsigned char sm_new[2 * D * 2];  // fused append
   WorkItem w = decode_work_item(p, blockIdx.x);
-  const Ranked rk = ranked_seq(p, w.seq, sm_hist, sm_pick);
+  Ranked rk;
+  if constexpr (M == kModeOrdered) {
+    // the caller's order; an entry outside the batch leaves its slot idle
+    rk.seq = p.order[w.seq];
+    if (rk.seq < 0 || rk.seq >= p.num_seqs) return;
+    rk.len = p.seq_lens[rk.seq];
+  } else {
+    rk = ranked_seq(p, w.seq, sm_hist, sm_pick);
+  }
   w.seq = rk.seq;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,15 +298,18 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t s
   const dim3 block(kWaves * 64);
   const int mode = p.block_stride != 0      ? kModeLayered
                    : p.new_slots != nullptr ? kModeFused
+                   : p.order != nullptr     ? kModeOrdered
                                             : kModePlain;
 #define PA_LAUNCH(DIM, MODE) decode_mfma_kernel<DIM, MODE><<<grid, block, 0, stream>>>(p)
   if (head_dim == 128) {
     if (mode == kModeLayered) PA_LAUNCH(128, kModeLayered);
     else if (mode == kModeFused) PA_LAUNCH(128, kModeFused);
+    else if (mode == kModeOrdered) PA_LAUNCH(128, kModeOrdered);
     else PA_LAUNCH(128, kModePlain);
   } else if (head_dim == 64) {
     if (mode == kModeLayered) PA_LAUNCH(64, kModeLayered);
     else if (mode == kModeFused) PA_LAUNCH(64, kModeFused);
+    else if (mode == kModeOrdered) PA_LAUNCH(64, kModeOrdered);
     else PA_LAUNCH(64, kModePlain);
   } else {
     return hipErrorInvalidValue;

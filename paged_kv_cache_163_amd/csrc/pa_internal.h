@@ -48,6 +48,10 @@ struct DecodeParams {
   int64_t layer_q_stride;
   int64_t layer_ws_stride;
   int32_t num_layers;           // grid extent along layers (1 without layering)
+  // Caller's processing order (a permutation of [0, num_seqs), longest
+  // sequence first): work item slot s serves sequence order[s].  Null: the
+  // kernel ranks the batch itself.
+  const int32_t* order;
 };
 
 // Everything a chunked-prefill launch needs.

@@ -64,6 +64,8 @@ _decode = _sig("pa_decode", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32
                _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp)
 _decode_ex = _sig("pa_decode_ex", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                   _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32, _vp)
+_decode_ordered = _sig("pa_decode_ordered", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32,
+                       _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32, _vp)
 _decode_append = _sig("pa_decode_append", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32,
                       _vp)
@@ -103,7 +105,7 @@ EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_appe
             "pa_bm_append_slots", "pa_bm_release", "pa_bm_swap_out", "pa_bm_swap_in",
             "pa_bm_decode_inputs", "pa_bm_sequence", "pa_bm_stats", "pa_bm_refcount",
             "pa_kv_append_layered", "pa_decode_layered", "pa_copy_blocks_layered",
-            "pa_swap_blocks_layered"]
+            "pa_swap_blocks_layered", "pa_decode_ordered"]
 
 
 def abi_version() -> int:
@@ -259,6 +261,32 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
                     _dev(v_cache, "v_cache", ndim=4), *common, float(scale), int(partition_size),
                     ws_ptr, ws_len, dt, KERNELS[kernel], _stream(stream))
     _check(st, "decode")
+    return out
+
+
+def longest_first(seq_lens) -> torch.Tensor:
+    """A longest-first processing order for pa_decode_ordered (host helper:
+    stable sort of the lengths, descending), as an int32 tensor on the lengths'
+    device."""
+    return torch.sort(seq_lens.to(torch.int64), descending=True, stable=True).indices.to(
+        torch.int32)
+
+
+def decode_ordered(q, k_cache, v_cache, block_tables, seq_lens, order, scale, max_seq_len=None,
+                   partition_size=0, out=None, workspace=None, kernel="auto", stream=None):
+    """decode() with a caller-kept processing order (see pa_decode_ordered)."""
+    if order.dim() != 1 or order.shape[0] != q.shape[0]:
+        raise ValueError("order must be [num_seqs]")
+    out, dt, common, ws_ptr, ws_len = _decode_common(
+        q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, partition_size, out,
+        workspace, kernel)
+    bt_ptr, maxblk, sl_ptr, mx, *rest = common
+    st = _decode_ordered(_dev(out, "out", ndim=3), _dev(q, "q", ndim=3),
+                         _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+                         bt_ptr, maxblk, sl_ptr, mx, _dev(order, "order", torch.int32), *rest,
+                         float(scale), int(partition_size), ws_ptr, ws_len, dt, KERNELS[kernel],
+                         _stream(stream))
+    _check(st, "decode_ordered")
     return out
 
 

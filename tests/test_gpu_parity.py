@@ -448,3 +448,28 @@ def test_longest_first_ranking_large_batches(pa, batch):
     rows = got[:, 0, :4]
     live = [s for s in range(batch) if lens[s] > 0]
     assert len({tuple(r) for r in rows[live]}) == len(live)
+
+
+def test_decode_with_caller_order(pa):
+    """pa_decode_ordered: longest-first and arbitrary permutations give the
+    oracle's outputs; an order entry outside the batch leaves its slot idle
+    (that sequence's output is unspecified, every other one is right)."""
+    w = W.llama70b(num_seqs=64, append=False)
+    d = upload(w)
+    seqs = sample_seqs(w, 16)
+    ref = oracle_decode(w, seqs=seqs)
+    for order in (pa.longest_first(d["lens"]), torch.randperm(64, dtype=torch.int32).to(DEV)):
+        out = pa.decode_ordered(d["q"], d["k"], d["v"], d["bt"], d["lens"], order, w.scale,
+                                max_seq_len=w.max_seq_len)
+        torch.cuda.synchronize()
+        assert_close(as_f64(out)[seqs], ref, "bf16", "ordered decode")
+    order = pa.longest_first(d["lens"]).clone()
+    skipped = int(order[5])
+    order[5] = 64                                      # outside the batch: slot 5 idles
+    out = torch.full_like(d["q"], 7.0)
+    pa.decode_ordered(d["q"], d["k"], d["v"], d["bt"], d["lens"], order, w.scale,
+                      max_seq_len=w.max_seq_len, out=out)
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    rest = [s for s in seqs if s != skipped]
+    assert_close(got[rest], oracle_decode(w, seqs=rest), "bf16", "ordered decode, idle slot")

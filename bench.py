@@ -37,10 +37,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/sec, 1 GPU"
-DECODE_KERNEL_SOURCES = ["paged_kv_cache_163_amd/csrc/decode_mfma.hip",
-                         "paged_kv_cache_163_amd/csrc/mfma_step.h",
-                         "paged_kv_cache_163_amd/csrc/pa_internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama70b_traffic.json")
+# Sources each profiled kernel is built from: a stored counter record is used
+# only while their hash still matches.
+KERNEL_SOURCES = {
+    "decode_mfma_kernel": ["paged_kv_cache_163_amd/csrc/decode_mfma.hip",
+                           "paged_kv_cache_163_amd/csrc/mfma_step.h",
+                           "paged_kv_cache_163_amd/csrc/pa_internal.h"],
+    "prefill_mfma_kernel": ["paged_kv_cache_163_amd/csrc/prefill_mfma.hip",
+                            "paged_kv_cache_163_amd/csrc/mfma_step.h",
+                            "paged_kv_cache_163_amd/csrc/pa_internal.h"],
+}
 
 
 def parse():
@@ -68,22 +74,24 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash() -> str:
+def source_hash(kernel: str = "decode_mfma_kernel") -> str:
     h = hashlib.sha256()
-    for rel in DECODE_KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_entry(workload: str):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
-    None when absent or taken on a different version of the kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_entry(workload: str, kernel: str = "decode_mfma_kernel"):
+    """HBM bytes per launch of `kernel` on `workload` from committed rocprofv3
+    counter runs, or None when absent or taken on a different version of the
+    kernel's sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel[:-len('_kernel')]}_{workload}_traffic.json")
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != source_hash() or rec.get("workload") != workload:
+    if rec.get("kernel_source_hash") != source_hash(kernel) or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -273,7 +281,7 @@ def prefill_main(args, np, torch, W, pa, dev):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic_entry(w.name, "prefill_mfma_kernel"),
             "kernel": "prefill_mfma_kernel",
             "flops_per_launch": flops,
             "avg_launch_ms": round(step_ms, 5),

@@ -12,7 +12,7 @@ then WRITE_SIZE, in KiB per dispatch) into HBM bytes per launch of KERNEL.
 Each counter is scaled by what it reads for a plain device copy of known size
 (``bench.py --copy-calibration``: 1 GiB read and 1 GiB written per launch),
 so the figure is in real bytes whatever unit or XCD coverage the counter has.
-The JSON record carries a hash of the decode kernel's sources; bench.py only
+The JSON record carries a hash of the kernel's sources; bench.py only
 reports it while the sources are unchanged.
 """
 
@@ -89,7 +89,7 @@ def main(argv):
         import bench
         rec = traffic(fd, wd, cfd, cwd, kernel)
         rec.update({"kernel": kernel, "workload": workload,
-                    "kernel_source_hash": bench.source_hash()})
+                    "kernel_source_hash": bench.source_hash(kernel)})
         with open(out_json, "w") as f:
             json.dump(rec, f, indent=1)
         with open(out_md, "w") as f:

@@ -455,7 +455,7 @@ def layered_main(args, np, torch, W, pa, dev, layers=8):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: this library runs on one GPU only (--gpus {args.gpus} requested); "
               "the decode path shards by sequence or KV head with no exchange, but no "
               "multi-GPU run is provided.", file=sys.stderr)
         sys.exit(2)

@@ -84,51 +84,82 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {  // round to nearest 
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// One 32-key step for all row tiles of a wave.  With kMask, keys > lim[nr]
-// (the lane's row position) are masked, unless the whole step lies at or
-// before kfull, the wave's first row position; V rows at or past kend are
-// zeroed.
+// Scores S^T = K Q^T of one 32-key step for every row tile of a wave, raw
+// (unscaled): s[nr][kt][j] is key 16 kt + 4 q4 + j of the step for the
+// lane's row of tile nr.  K: lane (r16, q4) reads staged row 16 kt + r16,
+// head dims 32 i + 8 q4 .. + 7, once for all row tiles.
+template <int D>
+__device__ inline void step_scores(f32x4 (&s)[kRowTiles][2], const unsigned char* ks,
+                                   const u32x4 (&qb)[kRowTiles][D / 32], int r16, int q4) {
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[nr][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const u32x4 k = *(const u32x4*)(ks + (16 * kt + r16) * kKvStride<D> + 64 * i + 16 * q4);
+#pragma unroll
+      for (int nr = 0; nr < kRowTiles; ++nr) s[nr][kt] = mma(k, qb[nr][i], s[nr][kt]);
+    }
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// The V^T operands of one step (A operands of the PV MFMAs).  Tile jt covers
+// head dims 16 jt .. 16 jt + 15: lane (r16, q4) holds d = 16 jt + r16 for the
+// step's keys tau(q4, e) = 16 (e / 4) + 4 q4 + e % 4, e = 0..7, the order
+// the score tiles leave P^T in.  The LDS transpose read (ds_read_b64_tr_b16)
+// hands lane 4 b + c of each 16-lane group element c of the 8-byte rows that
+// lanes b, b + 4, b + 8 and b + 12 of the group address; lane (r16, q4)
+// addresses key 4 q4 + r16 / 4 (16 more for the second read) at head dims
+// 16 jt + 4 (r16 % 4) .. + 3.
+template <int D>
+__device__ inline void read_v(u32x4 (&av)[D / 16], const unsigned char* vs, int r16, int q4) {
+  const unsigned char* v0 = vs + (4 * q4 + (r16 >> 2)) * kKvStride<D> + 8 * (r16 & 3);
+#pragma unroll
+  for (int jt = 0; jt < D / 16; ++jt) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * jt));
+    const i16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 16 * kKvStride<D> + 32 * jt));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+    av[jt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+}
+
+// Softmax and PV of one 32-key step for all row tiles of a wave, from its
+// raw scores s.  Keys > lim[nr] (the lane's row position) are masked unless
+// the whole step lies at or before kfull, the wave's first row position; V
+// values of keys at or past kend are zeroed.
 // c = scale * log2(e) > 0 (the host rejects other scales), so the row max of
 // c*s is c times the max of s.
-template <int D, bool kMask>
-__device__ inline void prefill_step(StepRegs<D>& r, PfAcc<D> (&a)[kRowTiles],
-                                    const u32x4 (&qb)[kRowTiles][D / 32], int base, int kend,
-                                    int kfull, const int (&lim)[kRowTiles], float c, int q4) {
-  constexpr int kKi = D / 32;
+template <int D>
+__device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&av)[D / 16],
+                                       PfAcc<D> (&a)[kRowTiles], int base, int kend, int kfull,
+                                       const int (&lim)[kRowTiles], float c, int q4) {
   constexpr int kVd = D / 16;
-  if (base + 32 > kend) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tok = base + 16 * (e >> 2) + 4 * q4 + (e & 3);
-      if (tok >= kend) r.v[e] = typename VRow<D>::T{};
-    }
-  }
-  // V^T operands of the step (token order tau(q4, e)), shared by the tiles
-  u32x4 av[kVd];
-#pragma unroll
-  for (int jt = 0; jt < kVd; ++jt) {
+  if (base + 32 > kend) {  // zero the V values of keys past the wave's last key
+    uint32_t keep[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t lo = r.v[2 * u][jt >> 1];
-      const uint32_t hi = r.v[2 * u + 1][jt >> 1];
-      av[jt][u] = (jt & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                           : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      const int tok = base + 16 * (u >> 1) + 4 * q4 + 2 * (u & 1);
+      keep[u] = (tok < kend ? 0x0000FFFFu : 0u) | (tok + 1 < kend ? 0xFFFF0000u : 0u);
     }
+#pragma unroll
+    for (int jt = 0; jt < kVd; ++jt)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) av[jt][u] &= keep[u];
   }
   const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr) {
-    f32x4 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < kKi; ++i) s[kt] = mma(r.k[kt][i], qb[nr][i], s[kt]);
-    }
     float sv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sv[e] = s[e >> 2][e & 3];
-    if (kMask && base + 31 > kfull) {  // wave-uniform: some row does not see the whole step
+    for (int e = 0; e < 8; ++e) sv[e] = s[nr][e >> 2][e & 3];
+    if (base + 31 > kfull) {  // wave-uniform: some row does not see the whole step
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = base + 16 * (e >> 2) + 4 * q4 + (e & 3);
@@ -220,38 +251,6 @@ template <int D>
 __device__ inline void stage_store(const Stage<D>& st, const StagePlan<D>& sp, unsigned char* buf) {
 #pragma unroll
   for (int j = 0; j < kStageParts<D>; ++j) *(u32x4*)(buf + sp.lds[j]) = st.part[j];
-}
-
-// A wave's MFMA operands of one step from the staged tiles (the layout the
-// register loads of mfma_step.h produce).
-template <int D>
-__device__ inline void read_step(StepRegs<D>& r, const unsigned char* buf, int r16, int q4) {
-  const unsigned char* ks = buf;
-  const unsigned char* vs = buf + 32 * kKvStride<D>;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-      r.k[kt][i] = *(const u32x4*)(ks + (16 * kt + r16) * kKvStride<D> + 64 * i + 16 * q4);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int tok = 16 * (e >> 2) + 4 * q4 + (e & 3);
-    r.v[e] = *(const typename VRow<D>::T*)(vs + tok * kKvStride<D> + r16 * (D / 16) * 2);
-  }
-}
-
-// A lane's part of one output row: head-dimension values [d0, d0 + D/16).
-template <int D>
-__device__ inline void store_row_part(uint16_t* dst, const float* v) {
-  constexpr int kVd = D / 16;
-  uint32_t w[kVd / 2];
-#pragma unroll
-  for (int j = 0; j < kVd / 2; ++j)
-    w[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
-  if constexpr (kVd == 8)
-    *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
-  else
-    *(u32x2*)dst = u32x2{w[0], w[1]};
 }
 
 template <int D>
@@ -358,9 +357,11 @@ void prefill_mfma_kernel(PrefillParams p) {
       const bool more = base + 32 < kend_wg;
       if (more) stage_load<D>(st, sp, c, base + 32, bad);  // in flight during the math
       if (base < kend) {
-        StepRegs<D> r;
-        read_step<D>(r, sm_kv[buf], r16, q4);
-        prefill_step<D, true>(r, a, qb, base, kend, kfull, lim, p.scale_log2, q4);
+        f32x4 s[kRowTiles][2];
+        step_scores<D>(s, sm_kv[buf], qb, r16, q4);
+        u32x4 av[D / 16];
+        read_v<D>(av, sm_kv[buf] + 32 * kKvStride<D>, r16, q4);
+        step_softmax_pv<D>(s, av, a, base, kend, kfull, lim, p.scale_log2, q4);
       }
       if (more) stage_store<D>(st, sp, sm_kv[buf ^ 1]);
       __syncthreads();
@@ -376,13 +377,13 @@ void prefill_mfma_kernel(PrefillParams p) {
     const int g = row - (row / G) * G;
     if (qi >= nq) continue;
     const float inv = bad ? __builtin_nanf("") : 1.0f / a[nr].l[0];
-    uint16_t* orow = out + (int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D;
+    // o[jt][rr] is head dim 16 jt + 4 q4 + rr of the lane's row
+    uint16_t* orow = out + (int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D + 4 * q4;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float v[kVd];
-#pragma unroll
-      for (int jt = 0; jt < kVd; ++jt) v[jt] = a[nr].o[jt][rr] * inv;
-      store_row_part<D>(orow + kVd * (4 * q4 + rr), v);
+    for (int jt = 0; jt < kVd; ++jt) {
+      const f32x4 o = a[nr].o[jt];
+      *(u32x2*)(orow + 16 * jt) = u32x2{pack_bf16(o[0] * inv, o[1] * inv),
+                                        pack_bf16(o[2] * inv, o[3] * inv)};
     }
   }
 }

@@ -67,6 +67,11 @@ def parse():
     ap.add_argument("--rank-in-kernel", action="store_true",
                     help="let every decode work-group rank the batch (pa_decode) instead of "
                          "passing the longest-first order the step keeps (pa_decode_ordered)")
+    ap.add_argument("--plain-decode", action="store_true",
+                    help="shared_prefix: time pa_decode instead of the shared-prefix decode "
+                         "(pa_decode_shared_prefix)")
+    ap.add_argument("--prefix-partition", type=int, default=0,
+                    help="shared_prefix: keys per prefix partition (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -513,7 +518,18 @@ def main():
     # Every decode step adds one token to every sequence, so the batch's
     # longest-first order holds from step to step: an engine computes it when
     # the batch changes, not per step.
-    ordered = not args.rank_in_kernel and not fused and plan.kernel == "mfma"
+    # Shared-prefix batch: every table starts with the same prefix blocks, so
+    # the shared-prefix decode attends them once for the whole group.
+    shared = ("prefix_blocks" in w.meta and not args.plain_decode and not fused
+              and args.kernel in ("auto", "mfma"))
+    if shared:
+        groups = ([0, w.num_seqs], [int(w.meta["prefix_blocks"])])
+        sp_bytes = pa.shared_prefix_workspace_bytes(
+            w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size, w.max_seq_len,
+            w.max_blocks_per_seq, *groups, prefix_partition_size=args.prefix_partition,
+            partition_size=args.partition)
+        ws = torch.empty(max(sp_bytes, 16), dtype=torch.uint8, device=dev)
+    ordered = not args.rank_in_kernel and not fused and not shared and plan.kernel == "mfma"
     order = pa.longest_first(lens) if ordered else None
 
     def step(i, ev=None):
@@ -528,6 +544,11 @@ def main():
             pa.decode_append(q, kc, vc, fk, fv, fslots, bt, lens, w.scale,
                              max_seq_len=w.max_seq_len, partition_size=args.partition, out=out,
                              workspace=ws, kernel=args.kernel)
+        elif shared:
+            pa.decode_shared_prefix(q, kc, vc, bt, lens, w.scale, *groups,
+                                    max_seq_len=w.max_seq_len,
+                                    prefix_partition_size=args.prefix_partition,
+                                    partition_size=args.partition, out=out, workspace=ws)
         elif ordered:
             pa.decode_ordered(q, kc, vc, bt, lens, order, w.scale, max_seq_len=w.max_seq_len,
                               partition_size=args.partition, out=out, workspace=ws,
@@ -556,15 +577,22 @@ def main():
     timer.close()
 
     kv_bytes = W.decode_kv_bytes(w.seq_lens, w.kv_heads, w.head_dim, w.elem_bytes)
+    # K/V bytes of distinct live (block, slot) positions: what one pass over
+    # the pool must read when tables share blocks (equal to kv_bytes otherwise)
+    unique_bytes = W.unique_kv_bytes(w.block_tables, w.seq_lens, w.block_size, w.kv_heads,
+                                     w.head_dim, w.elem_bytes)
     total_alg = (kv_bytes + 2 * w.q.nbytes + 4 * int(sum(-(-int(n) // w.block_size)
                                                         for n in w.seq_lens)) + 4 * w.num_seqs)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
     kernel_name = f"decode_{plan.kernel}_kernel" + (" (fused append)" if fused else "")
     split_reduce = plan.kernel != "stream" and nparts > 1
+    if shared:
+        kernel_name = "prefix_attend_kernel + decode_mfma_kernel (tails) + prefix_merge_kernel"
+        split_reduce = False
     dec_avg = float(dec_ms.mean())
-    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
+    achieved = unique_bytes / (dec_avg * 1e-3) / 1e9
     # the stored counter record is for the plain decode kernel at the default plan
-    plain = args.partition == 0 and args.kernel == "auto" and not fused
+    plain = args.partition == 0 and args.kernel == "auto" and not fused and not shared
     traffic = traffic_entry(w.name) if plain else None
 
     line = {
@@ -593,7 +621,12 @@ def main():
             "appended_tokens": int(w.slot_mapping.shape[0]),
             "append": "fused into the decode launch" if fused else "pa_kv_append launch",
             "order": ("longest-first, kept across steps (pa_decode_ordered)" if ordered
+                      else "index order (shared-prefix decode)" if shared
                       else "ranked inside the kernel"),
+            "shared_prefix": ({"call": "pa_decode_shared_prefix", "groups": groups[0],
+                               "prefix_blocks": groups[1],
+                               "prefix_partition": args.prefix_partition or "library's choice"}
+                              if shared else None),
             "cow_pairs": int(w.cow_pairs.shape[0]),
             "kernel": plan.kernel,
             "partition_size": eff_p,
@@ -606,6 +639,7 @@ def main():
         "decode_ms": {"mean": round(dec_avg, 5), "median": round(float(np.median(dec_ms)), 5),
                       "min": round(float(dec_ms.min()), 5)},
         "kv_bytes_per_step": kv_bytes,
+        "unique_kv_bytes_per_step": unique_bytes,
         "total_algorithmic_bytes_per_decode": total_alg,
         "roofline": {
             "bound": "hbm",
@@ -615,7 +649,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": kernel_name + (" + decode_reduce_kernel" if split_reduce else ""),
-            "bytes_per_launch": kv_bytes,
+            "bytes_per_launch": unique_bytes,
             "avg_launch_ms": round(dec_avg, 5),
         },
         "cpu_baseline": None,

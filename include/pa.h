@@ -259,6 +259,67 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
                            int32_t dtype, int32_t kernel, void* stream);
 
 /*
+ * Shared-prefix decode: the result of pa_decode for a batch in which groups of
+ * sequences share the leading blocks of their tables (one prefix, refcounted,
+ * N tables pointing at it: "How PagedAttention works", section "A strong
+ * answer", the shared system prompt across 200 conversations; lihaoran.work
+ * explainer, section "Shared prefixes need matching computation").  Every
+ * member's query attends the shared keys in one matrix-core pass per group,
+ * which reads each shared K/V tile once per work-group instead of once per
+ * sequence; the positions after the prefix run through the decode kernel, and
+ * a merge kernel combines the two softmax partials.  Outputs equal pa_decode's
+ * up to rounding.
+ *
+ *   group_start          HOST int32 [num_groups + 1], non-decreasing, in
+ *                        [0, num_seqs]: group g is sequences
+ *                        group_start[g] .. group_start[g+1]-1 (order the batch
+ *                        so that each group's members are adjacent)
+ *   group_prefix_blocks  HOST int32 [num_groups]: the number of leading table
+ *                        entries every member of group g shares with its
+ *                        first member (the leader); whole blocks only, so the
+ *                        prefix is group_prefix_blocks[g] * block_size tokens
+ *   num_groups           0 .. PA_MAX_PREFIX_GROUPS (0: plain decode)
+ *   prefix_partition_size  keys per prefix-kernel partition (rounded up to a
+ *                        multiple of 32); 0 = the library's choice (about two
+ *                        work-groups per compute unit)
+ *   partition_size       tail partitions, as in pa_decode (0 = default)
+ *   workspace            device, >= pa_decode_shared_prefix_workspace_bytes()
+ *                        with the same arguments, 16-byte aligned
+ * Sequences outside every group, and groups with no member or no shared
+ * block, decode as in pa_decode.  A member whose table does not start with
+ * its leader's group_prefix_blocks entries, or whose length is below the
+ * prefix, gets a NaN row (checked on the device); other device contents as in
+ * pa_decode.  Requirements: bf16, the matrix-core kernel's shapes
+ * (head_dim in {64, 128}, block_size a power of two in [16, 256]) with
+ * G = num_heads / kv_heads a power of two <= 16, and scale > 0 (the prefix
+ * kernel scales row maxima of raw scores); a group's prefix may not exceed
+ * max_blocks_per_seq blocks or max_seq_len tokens.  Errors: bad host
+ * arguments -> PA_ERR_INVALID_ARG; more than PA_MAX_PREFIX_GROUPS groups or
+ * an unsupported shape -> PA_ERR_UNSUPPORTED.  Three launches on `stream`
+ * (prefix attention, tail decode, merge); allocates nothing.
+ */
+#define PA_MAX_PREFIX_GROUPS 32
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t max_seq_len, int32_t num_seqs, int32_t num_heads,
+                                  int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, const int32_t* group_start,
+                                  const int32_t* group_prefix_blocks, int32_t num_groups,
+                                  int32_t prefix_partition_size, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, int32_t dtype,
+                                  void* stream);
+
+/* Workspace bytes pa_decode_shared_prefix needs for these arguments (0 when
+ * they are invalid or unsupported, or when nothing is shared and the plain
+ * decode needs none). */
+size_t pa_decode_shared_prefix_workspace_bytes(
+    int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_seq_len, int32_t max_blocks_per_seq, const int32_t* group_start,
+    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t prefix_partition_size,
+    int32_t partition_size, int32_t dtype);
+
+/*
  * Copy-on-write block copy: for each (src, dst) pair, copy every KV head and
  * every slot of physical block src into physical block dst, in both caches
  * ("How PagedAttention works", feature table row on beam search and parallel

@@ -133,7 +133,11 @@ __device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_his
 // kModePlain: one per-layer pool.  kModeFused: plus the step's append.
 // kModeLayered: one or more layers of a layered pool (layer = blockIdx.y).
 // kModeOrdered: a per-layer pool with the caller's longest-first order.
-enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered };
+// kModeTail: shared-prefix decode; each sequence's partitions start after
+// its group's shared prefix (prefix_attend covers the prefix), index order,
+// and every partial goes to the workspace unless the sequence has no prefix
+// and one partition.
+enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered, kModeTail };
 
 template <int D, int M>
 __global__ __launch_bounds__(kWaves * 64)
@@ -156,6 +160,9 @@ void decode_mfma_kernel(DecodeParams p) {
     rk.seq = p.order[w.seq];
     if (rk.seq < 0 || rk.seq >= p.num_seqs) return;
     rk.len = p.seq_lens[rk.seq];
+  } else if constexpr (M == kModeTail) {
+    rk.seq = w.seq;
+    rk.len = p.seq_lens[w.seq];
   } else {
     rk = ranked_seq(p, w.seq, sm_hist, sm_pick);
   }
@@ -194,10 +201,13 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     return;
   }
-  const int pstart = w.part * p.partition_size;
+  // Shared-prefix decode: positions before `pfx` belong to the prefix kernel.
+  int pfx = 0;
+  if constexpr (M == kModeTail) pfx = shared_prefix_tokens(p.prefix, w.seq);
+  const int pstart = pfx + w.part * p.partition_size;
   if (pstart >= len) return;
   const int pend = min(len, pstart + p.partition_size);
-  const int nparts = ceil_div_i(len, p.partition_size);
+  const int nparts = ceil_div_i(len - pfx, p.partition_size);
   // Fused append: the partition that holds the new token (position len - 1,
   // so the last one) masks it out of the step math and folds it in from the
   // new row afterwards; partition 0 writes it to its cache slot at the very
@@ -276,10 +286,11 @@ void decode_mfma_kernel(DecodeParams p) {
     const int d = i - g * D;
     float mx, l, o;
     merge_waves<D, kWaves>(sm_o, sm_m, sm_l, g, d, mx, l, o);
-    if (nparts == 1) {
+    if (nparts == 1 && pfx == 0) {
       out[(out_row0 + g) * D + d] = f32_to_bf16(o / l);
     } else {
-      const int64_t slot = (out_row0 + g) * p.num_partitions + w.part;
+      const int part_slot = M == kModeTail ? p.prefix.parts + w.part : w.part;
+      const int64_t slot = (out_row0 + g) * p.num_partitions + part_slot;
       ws_o[slot * D + d] = o;
       if (d == 0) {
         ws_ml[slot * 2 + 0] = mx;
@@ -293,10 +304,13 @@ void decode_mfma_kernel(DecodeParams p) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.num_partitions * p.num_seqs * p.kv_heads),
+  // shared-prefix decode: the grid covers the tail partitions only
+  const int64_t parts = p.num_partitions - p.prefix.parts;
+  const dim3 grid((unsigned)(parts * p.num_seqs * p.kv_heads),
                   (unsigned)(p.num_layers > 1 ? p.num_layers : 1));
   const dim3 block(kWaves * 64);
-  const int mode = p.block_stride != 0      ? kModeLayered
+  const int mode = p.prefix.num_groups > 0 ? kModeTail
+                   : p.block_stride != 0      ? kModeLayered
                    : p.new_slots != nullptr ? kModeFused
                    : p.order != nullptr     ? kModeOrdered
                                             : kModePlain;
@@ -305,11 +319,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t s
     if (mode == kModeLayered) PA_LAUNCH(128, kModeLayered);
     else if (mode == kModeFused) PA_LAUNCH(128, kModeFused);
     else if (mode == kModeOrdered) PA_LAUNCH(128, kModeOrdered);
+    else if (mode == kModeTail) PA_LAUNCH(128, kModeTail);
     else PA_LAUNCH(128, kModePlain);
   } else if (head_dim == 64) {
     if (mode == kModeLayered) PA_LAUNCH(64, kModeLayered);
     else if (mode == kModeFused) PA_LAUNCH(64, kModeFused);
     else if (mode == kModeOrdered) PA_LAUNCH(64, kModeOrdered);
+    else if (mode == kModeTail) PA_LAUNCH(64, kModeTail);
     else PA_LAUNCH(64, kModePlain);
   } else {
     return hipErrorInvalidValue;

@@ -187,6 +187,85 @@ Residency residency(const void* ptr, const void** kernel_ptr) {
   return kUnknown;  // pageable host memory or a type a kernel cannot address
 }
 
+// Shared-prefix decode plan: the tail decode's plan on the matrix-core kernel
+// (partitions over the positions after the prefix) plus the prefix
+// partitions.  The prefix keys are split until the prefix kernel offers about
+// two work-groups per compute unit (kPrefixWgsPerCu); prefix_partition_size
+// > 0 fixes the split instead.  Groups with no member or no shared block
+// share nothing.
+constexpr int32_t kPrefixWgsPerCu = 2;
+static_assert(pa::kMaxPrefixGroups == PA_MAX_PREFIX_GROUPS, "group limit");
+
+pa_status shared_prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                             int32_t max_blocks_per_seq, const int32_t* group_start,
+                             const int32_t* group_prefix_blocks, int32_t num_groups,
+                             int32_t prefix_partition_size, int32_t partition_size, int32_t dtype,
+                             Plan* plan, pa::PrefixGroups* pg) {
+  Plan tail;
+  const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
+                                 max_seq_len, partition_size, dtype, PA_KERNEL_MFMA, &tail);
+  if (st != PA_OK) return st;
+  if (num_groups < 0 || prefix_partition_size < 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_groups > pa::kMaxPrefixGroups) return PA_ERR_UNSUPPORTED;
+  const int32_t group = num_heads / kv_heads;
+  if (!pow2(group) || group > 16) return PA_ERR_UNSUPPORTED;  // 128 / group members per tile
+  memset(pg, 0, sizeof(*pg));
+  if (num_groups > 0) {
+    if (group_start == nullptr || group_prefix_blocks == nullptr) return PA_ERR_INVALID_ARG;
+    if (group_start[0] < 0) return PA_ERR_INVALID_ARG;
+    for (int32_t g = 0; g < num_groups; ++g) {
+      const int64_t blocks = group_prefix_blocks[g];
+      if (group_start[g + 1] < group_start[g] || group_start[g + 1] > num_seqs || blocks < 0 ||
+          blocks > max_blocks_per_seq || blocks * block_size > max_seq_len)
+        return PA_ERR_INVALID_ARG;
+    }
+  }
+  // work-groups of the prefix kernel without splitting the keys
+  int64_t base = 0, max_tokens = 0;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int64_t members = group_start[g + 1] - group_start[g];
+    const int64_t tokens = (int64_t)group_prefix_blocks[g] * block_size;
+    if (members == 0 || tokens == 0) continue;
+    base += ceil_div(members * group, pa::kPrefillRows) * kv_heads;
+    if (tokens > max_tokens) max_tokens = tokens;
+  }
+  *plan = tail;
+  if (max_tokens == 0) return PA_OK;  // nothing shared: the plain decode
+  int64_t part;
+  if (prefix_partition_size > 0) {
+    part = round_up(prefix_partition_size, kMfmaStep);
+  } else {
+    const int64_t target = (int64_t)kPrefixWgsPerCu * device_cus();
+    const int64_t splits = base >= target ? 1 : target / base;
+    part = round_up(ceil_div(max_tokens, splits), kMfmaStep);
+  }
+  const int64_t parts = ceil_div(max_tokens, part);
+  const int64_t slots = parts + tail.partitions;
+  if (slots > kMaxPartitions || (int64_t)group * slots * 4 > 64 * 1024) return PA_ERR_UNSUPPORTED;
+  pg->num_groups = num_groups;
+  pg->partition = (int32_t)part;
+  pg->parts = (int32_t)parts;
+  int64_t wgs = 0;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int64_t members = group_start[g + 1] - group_start[g];
+    const int64_t tokens = (int64_t)group_prefix_blocks[g] * block_size;
+    pg->start[g] = group_start[g];
+    pg->tokens[g] = members > 0 ? (int32_t)tokens : 0;
+    pg->wg_start[g] = (int32_t)wgs;
+    if (members > 0 && tokens > 0)
+      wgs += round_up(kv_heads * ceil_div(tokens, part), 8) *
+             ceil_div(members * group, pa::kPrefillRows);
+    if (wgs > INT32_MAX) return PA_ERR_INVALID_ARG;
+  }
+  pg->start[num_groups] = group_start[num_groups];
+  pg->wg_start[num_groups] = (int32_t)wgs;
+  plan->partitions = (int32_t)slots;
+  plan->workspace = (size_t)num_seqs * num_heads * slots * (head_dim + 2) * 4;
+  return PA_OK;
+}
+
 }  // namespace
 
 // Decode over layers of a layered pool: k_cache / v_cache point at the first
@@ -418,6 +497,81 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                       max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
                       num_blocks, scale, partition_size, workspace, workspace_bytes, dtype,
                       PA_KERNEL_AUTO, stream);
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t max_seq_len, int32_t num_seqs, int32_t num_heads,
+                                  int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, const int32_t* group_start,
+                                  const int32_t* group_prefix_blocks, int32_t num_groups,
+                                  int32_t prefix_partition_size, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, int32_t dtype,
+                                  void* stream) {
+  Plan plan;
+  pa::PrefixGroups pg;
+  const pa_status st = shared_prefix_plan(
+      num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len, max_blocks_per_seq,
+      group_start, group_prefix_blocks, num_groups, prefix_partition_size, partition_size, dtype,
+      &plan, &pg);
+  if (st != PA_OK) return st;
+  if (pg.num_groups == 0)  // nothing shared
+    return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                       max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
+                       num_blocks, scale, partition_size, workspace, workspace_bytes, dtype,
+                       PA_KERNEL_MFMA, stream, nullptr, nullptr, nullptr);
+  // the prefix kernel scales row maxima of raw scores, so scale must be > 0
+  if (num_blocks <= 0 || !isfinite(scale) || !(scale > 0.0f)) return PA_ERR_INVALID_ARG;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < plan.workspace || !aligned(workspace, 16))
+    return PA_ERR_INVALID_ARG;
+
+  pa::DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.ws_o = (float*)workspace;
+  p.ws_ml = p.ws_o + (size_t)num_seqs * num_heads * plan.partitions * head_dim;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.kv_heads = kv_heads;
+  p.group = num_heads / kv_heads;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.block_shift = log2i(block_size);
+  p.partition_size = plan.partition;
+  p.num_partitions = plan.partitions;
+  p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  p.num_layers = 1;
+  p.prefix = pg;
+  const hipStream_t s = (hipStream_t)stream;
+  if (pa::launch_prefix_attend(p, head_dim, s) != hipSuccess) return PA_ERR_HIP;
+  if (pa::launch_decode_mfma(p, head_dim, s) != hipSuccess) return PA_ERR_HIP;
+  return from_hip(pa::launch_prefix_merge(p, head_dim, s));
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(
+    int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_seq_len, int32_t max_blocks_per_seq, const int32_t* group_start,
+    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t prefix_partition_size,
+    int32_t partition_size, int32_t dtype) {
+  Plan plan;
+  pa::PrefixGroups pg;
+  if (shared_prefix_plan(num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len,
+                         max_blocks_per_seq, group_start, group_prefix_blocks, num_groups,
+                         prefix_partition_size, partition_size, dtype, &plan, &pg) != PA_OK)
+    return 0;
+  return plan.workspace;
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,

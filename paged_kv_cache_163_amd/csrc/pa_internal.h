@@ -7,6 +7,40 @@
 
 namespace pa {
 
+// Shared-prefix decode: groups of consecutive sequences whose block tables
+// start with the same physical blocks (one prefix, refcounted, many tables).
+// Group g is sequences start[g] .. start[g+1] - 1; each of them shares the
+// first tokens[g] / block_size table entries of sequence start[g] (its
+// leader).  The prefix kernel attends every member's query over the shared
+// keys once per group, in `parts` partitions of `partition` keys; the tail
+// decode covers each member's positions [tokens[g], seq_len).  Carried in the
+// kernel arguments (host arrays), so it costs no device memory.
+constexpr int kMaxPrefixGroups = 32;
+struct PrefixGroups {
+  int32_t num_groups;           // 0: no sharing (every other decode launch)
+  int32_t partition;            // prefix keys per prefix partition (a multiple of 32)
+  int32_t parts;                // workspace slots of prefix partials per row (max over groups)
+  int32_t start[kMaxPrefixGroups + 1];
+  int32_t tokens[kMaxPrefixGroups];    // shared prefix tokens (whole blocks)
+  int32_t wg_start[kMaxPrefixGroups + 1];  // prefix kernel: first work-group of each group
+};
+
+// Shared prefix tokens of sequence `seq` (0 outside every group).
+__device__ inline int shared_prefix_tokens(const PrefixGroups& g, int seq) {
+  int t = 0;
+  for (int i = 0; i < g.num_groups; ++i)
+    if (seq >= g.start[i] && seq < g.start[i + 1]) t = g.tokens[i];
+  return t;
+}
+
+// Group of sequence `seq`, or -1.
+__device__ inline int shared_prefix_group(const PrefixGroups& g, int seq) {
+  int r = -1;
+  for (int i = 0; i < g.num_groups; ++i)
+    if (seq >= g.start[i] && seq < g.start[i + 1]) r = i;
+  return r;
+}
+
 // Everything a decode launch needs, passed by value as the kernel argument.
 struct DecodeParams {
   void* out;                    // [B][Hq][D] dtype
@@ -52,6 +86,11 @@ struct DecodeParams {
   // sequence first): work item slot s serves sequence order[s].  Null: the
   // kernel ranks the batch itself.
   const int32_t* order;
+  // Shared-prefix decode (pa_decode_shared_prefix): the tail mode of the
+  // matrix-core kernel starts each sequence after its shared prefix and
+  // writes partials to slots prefix.parts + partition; the prefix kernel
+  // writes slots [0, prefix.parts).  num_partitions counts both.
+  PrefixGroups prefix;
 };
 
 // Everything a chunked-prefill launch needs.
@@ -204,5 +243,14 @@ hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t
 // Merges the per-partition partials of sequences with more than one partition.
 hipError_t launch_decode_reduce(const DecodeParams& p, bool is_bf16, int head_dim,
                                 hipStream_t stream);
+
+// Shared-prefix decode, bf16, head_dim in {64, 128}, group a power of two
+// <= 16: attention of every group member's query over the group's shared
+// keys (grid: p.prefix.wg_start[num_groups] work-groups), partials to the
+// workspace.
+hipError_t launch_prefix_attend(const DecodeParams& p, int head_dim, hipStream_t stream);
+// Merge of prefix and tail partials, one work-group per (sequence, KV head);
+// also checks that members' tables start with their leader's blocks.
+hipError_t launch_prefix_merge(const DecodeParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace pa

@@ -253,6 +253,40 @@ __device__ inline void stage_store(const Stage<D>& st, const StagePlan<D>& sp, u
   for (int j = 0; j < kStageParts<D>; ++j) *(u32x4*)(buf + sp.lds[j]) = st.part[j];
 }
 
+// The work-group's walk over keys [kstart, kend_wg) in 32-key steps (kstart
+// a multiple of 32): every thread stages its parts of the next step's K and V
+// tiles from HBM while the waves compute the current one from LDS (two
+// buffers, one barrier per step).  A wave takes the math of the steps below
+// its own kend only; every wave stages and meets every barrier.
+template <int D>
+__device__ inline void attend_keys(PfAcc<D> (&a)[kRowTiles], const SeqView& c,
+                                   const u32x4 (&qb)[kRowTiles][D / 32],
+                                   const int (&lim)[kRowTiles], int kstart, int kend_wg, int kend,
+                                   int kfull, float scale_log2, bool& bad,
+                                   unsigned char (*sm_kv)[2 * 32 * kKvStride<D>], int tid, int r16,
+                                   int q4) {
+  const StagePlan<D> sp = stage_plan<D>(c, tid);
+  Stage<D> st;
+  stage_load<D>(st, sp, c, kstart, bad);
+  stage_store<D>(st, sp, sm_kv[0]);
+  __syncthreads();
+  int buf = 0;
+  for (int base = kstart; base < kend_wg; base += 32) {
+    const bool more = base + 32 < kend_wg;
+    if (more) stage_load<D>(st, sp, c, base + 32, bad);  // in flight during the math
+    if (base < kend) {
+      f32x4 s[kRowTiles][2];
+      step_scores<D>(s, sm_kv[buf], qb, r16, q4);
+      u32x4 av[D / 16];
+      read_v<D>(av, sm_kv[buf] + 32 * kKvStride<D>, r16, q4);
+      step_softmax_pv<D>(s, av, a, base, kend, kfull, lim, scale_log2, q4);
+    }
+    if (more) stage_store<D>(st, sp, sm_kv[buf ^ 1]);
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_mfma_kernel(PrefillParams p) {
@@ -344,7 +378,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     a[nr].m = -INFINITY;
   }
   bool bad = false;
-
+  // The key loop of attend_keys, written out.
   __shared__ __attribute__((aligned(16))) unsigned char sm_kv[2][2 * 32 * kKvStride<D>];
   {
     const StagePlan<D> sp = stage_plan<D>(c, tid);
@@ -388,6 +422,119 @@ void prefill_mfma_kernel(PrefillParams p) {
   }
 }
 
+// Shared-prefix decode, prefix part: the decode queries of every member of a
+// group (sequences whose tables start with the same physical blocks) attend
+// the group's shared keys once per work-group instead of once per sequence
+// ("How PagedAttention works", section "A strong answer": one set of prefix
+// blocks with N tables pointing at it).  Rows are (member, query head) pairs
+// of one KV head, 128 per work-group, over one partition of the prefix keys;
+// no causal limit applies, since every member's position is past its prefix.
+// The result is a partial (unnormalised O, reference max m, sum l) in
+// workspace slot `partition` of the row, merged with the tail partials by
+// prefix_merge.
+//
+// Work order: group g owns work-groups wg_start[g] ..; inside it, all member
+// tiles of one (partition, KV head) pair run on one XCD (work-group x runs on
+// XCD x % 8), so the pair's K/V tiles stay in that XCD's L2.
+template <int D>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefix_attend_kernel(DecodeParams p) {
+  constexpr int kVd = D / 16;
+  const PrefixGroups& pg = p.prefix;
+  const int x = blockIdx.x;
+  int grp = 0;
+  for (int i = 1; i < pg.num_groups; ++i)
+    if (x >= pg.wg_start[i]) grp = i;
+  const int local = x - pg.wg_start[grp];
+  const int first = pg.start[grp];
+  const int members = pg.start[grp + 1] - first;
+  const int tokens = pg.tokens[grp];
+  const int G = p.group;
+  const int tiles = ceil_div_i(members * G, kPrefillRows);
+  const int combos = p.kv_heads * ceil_div_i(tokens, pg.partition);
+  const int slot = local >> 3;
+  const int combo = (slot / tiles) * 8 + (local & 7);
+  if (combo >= combos) return;
+  const int tile = slot - (slot / tiles) * tiles;
+  const int head = combo % p.kv_heads;
+  const int kp = combo / p.kv_heads;
+  const int kstart = kp * pg.partition;
+  const int kend_wg = min(tokens, kstart + pg.partition);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int m0 = tile * (kPrefillRows / G);  // first member of the work-group
+  const int wrow0 = wave * kWaveRows;
+  const bool wave_rows = m0 + wrow0 / G < members;
+  // every row sees every key of the partition: the mask only cuts the last
+  // step at kend_wg
+  const int kend = wave_rows ? kend_wg : kstart;
+  const int kfull = kend_wg - 1;
+
+  u32x4 qb[kRowTiles][D / 32];
+  int lim[kRowTiles];
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+    const int row = wrow0 + 16 * nr + r16;
+    const int mi = m0 + row / G;
+    const int g = row - (row / G) * G;
+    const bool valid = mi < members;
+    lim[nr] = kend_wg - 1;
+    const char* qrow = (const char*)p.q +
+                       (((int64_t)(first + mi) * p.num_heads + (int64_t)head * G + g) * D) * 2 +
+                       q4 * 16;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+      qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  SeqView c;
+  const int64_t head_stride = (int64_t)p.block_size * D * 2;
+  c.kbase = (const char*)p.k_cache + (int64_t)head * head_stride;
+  c.vbase = (const char*)p.v_cache + (int64_t)head * head_stride;
+  c.table = p.block_tables + (int64_t)first * p.max_blocks_per_seq;  // the leader's row
+  c.block_stride = (int64_t)p.kv_heads * head_stride;
+  c.nblocks_valid = tokens >> p.block_shift;
+  c.num_blocks = p.num_blocks;
+  c.block_shift = p.block_shift;
+  c.bmask = p.block_size - 1;
+
+  PfAcc<D> a[kRowTiles];
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+#pragma unroll
+    for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    a[nr].l = f32x4{0.f, 0.f, 0.f, 0.f};
+    a[nr].m = -INFINITY;
+  }
+  bool bad = false;
+  __shared__ __attribute__((aligned(16))) unsigned char sm_kv[2][2 * 32 * kKvStride<D>];
+  attend_keys<D>(a, c, qb, lim, kstart, kend_wg, kend, kfull, p.scale_log2, bad, sm_kv, tid,
+                 r16, q4);
+  if (!wave_rows) return;
+
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+    const int row = wrow0 + 16 * nr + r16;
+    const int mi = m0 + row / G;
+    const int g = row - (row / G) * G;
+    if (mi >= members) continue;
+    const int64_t wslot =
+        ((int64_t)(first + mi) * p.num_heads + (int64_t)head * G + g) * p.num_partitions + kp;
+    // o[jt][rr] is head dim 16 jt + 4 q4 + rr of the lane's row
+    float* orow = p.ws_o + wslot * D + 4 * q4;
+#pragma unroll
+    for (int jt = 0; jt < kVd; ++jt) *(f32x4*)(orow + 16 * jt) = a[nr].o[jt];
+    if (q4 == 0) {
+      p.ws_ml[wslot * 2 + 0] = a[nr].m;
+      p.ws_ml[wslot * 2 + 1] = bad ? __builtin_nanf("") : a[nr].l[0];  // a bad table: NaN rows
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t stream) {
@@ -398,6 +545,19 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t
     prefill_mfma_kernel<128><<<grid, block, 0, stream>>>(p);
   else if (head_dim == 64)
     prefill_mfma_kernel<64><<<grid, block, 0, stream>>>(p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_attend(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  const int wgs = p.prefix.wg_start[p.prefix.num_groups];
+  if (wgs <= 0) return hipSuccess;
+  const dim3 block(kPfWaves * 64);
+  if (head_dim == 128)
+    prefix_attend_kernel<128><<<dim3(wgs), block, 0, stream>>>(p);
+  else if (head_dim == 64)
+    prefix_attend_kernel<64><<<dim3(wgs), block, 0, stream>>>(p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -69,6 +69,11 @@ _decode_ordered = _sig("pa_decode_ordered", _i32, _vp, _vp, _vp, _vp, _vp, _i32,
 _decode_append = _sig("pa_decode_append", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32,
                       _vp)
+_decode_shared_prefix = _sig("pa_decode_shared_prefix", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                            _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _i32,
+                            _i32, _vp, _sz, _i32, _vp)
+_shared_prefix_ws = _sig("pa_decode_shared_prefix_workspace_bytes", _sz, _i32, _i32, _i32, _i32,
+                         _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32)
 _copy_blocks = _sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
 _P = ctypes.POINTER
 _bm_create = _sig("pa_bm_create", _i32, _i64, _i32, _i64, _i64, _P(_vp))
@@ -105,7 +110,9 @@ EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_appe
             "pa_bm_append_slots", "pa_bm_release", "pa_bm_swap_out", "pa_bm_swap_in",
             "pa_bm_decode_inputs", "pa_bm_sequence", "pa_bm_stats", "pa_bm_refcount",
             "pa_kv_append_layered", "pa_decode_layered", "pa_copy_blocks_layered",
-            "pa_swap_blocks_layered", "pa_decode_ordered"]
+            "pa_swap_blocks_layered", "pa_decode_ordered", "pa_decode_shared_prefix",
+            "pa_decode_shared_prefix_workspace_bytes"]
+MAX_PREFIX_GROUPS = 32
 
 
 def abi_version() -> int:
@@ -287,6 +294,64 @@ def decode_ordered(q, k_cache, v_cache, block_tables, seq_lens, order, scale, ma
                          float(scale), int(partition_size), ws_ptr, ws_len, dt, KERNELS[kernel],
                          _stream(stream))
     _check(st, "decode_ordered")
+    return out
+
+
+def _host_groups(group_start, group_prefix_blocks):
+    starts = [int(x) for x in group_start]
+    blocks = [int(x) for x in group_prefix_blocks]
+    if len(starts) != len(blocks) + 1:
+        raise ValueError("group_start needs one entry more than group_prefix_blocks")
+    n = len(blocks)
+    return ((_i32 * (n + 1))(*starts), (_i32 * max(n, 1))(*(blocks or [0])), n)
+
+
+def shared_prefix_workspace_bytes(num_seqs, num_heads, kv_heads, head_dim, block_size,
+                                  max_seq_len, max_blocks_per_seq, group_start,
+                                  group_prefix_blocks, prefix_partition_size=0,
+                                  partition_size=0, dtype=torch.bfloat16) -> int:
+    """Workspace bytes of decode_shared_prefix (pa_decode_shared_prefix_workspace_bytes)."""
+    gs, gb, n = _host_groups(group_start, group_prefix_blocks)
+    code = PA_BF16 if dtype == torch.bfloat16 else PA_F32
+    return int(_shared_prefix_ws(num_seqs, num_heads, kv_heads, head_dim, block_size, max_seq_len,
+                                 max_blocks_per_seq, gs, gb, n, prefix_partition_size,
+                                 partition_size, code))
+
+
+def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, scale, group_start,
+                         group_prefix_blocks, max_seq_len=None, prefix_partition_size=0,
+                         partition_size=0, out=None, workspace=None, stream=None):
+    """decode() for a batch whose groups of adjacent sequences share the leading
+    blocks of their tables (see pa_decode_shared_prefix).
+
+    ``group_start`` (host ints, length num_groups + 1) delimits the groups;
+    ``group_prefix_blocks`` (host ints) gives each group's shared leading
+    table entries.  The result equals decode() up to rounding.
+    """
+    gs, gb, n = _host_groups(group_start, group_prefix_blocks)
+    dt = _dtype_code(q)
+    B, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
+    maxblk = int(block_tables.shape[1])
+    ws_bytes = int(_shared_prefix_ws(B, hq, hkv, d, bs, int(max_seq_len), maxblk, gs, gb, n,
+                                     int(prefix_partition_size), int(partition_size), dt))
+    if out is None:
+        out = torch.empty_like(q)
+    if ws_bytes > 0 and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _decode_shared_prefix(
+        _dev(out, "out", ndim=3), _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
+        _dev(v_cache, "v_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32), maxblk,
+        _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), B, hq, hkv, d, bs, nb,
+        float(scale), gs, gb, n, int(prefix_partition_size), int(partition_size), ws_ptr, ws_len,
+        dt, _stream(stream))
+    _check(st, "decode_shared_prefix")
     return out
 
 

@@ -213,6 +213,20 @@ def decode_kv_bytes(seq_lens, kv_heads: int, head_dim: int, elem_bytes: int) -> 
 # generic builder
 # --------------------------------------------------------------------------
 
+def unique_kv_bytes(block_tables, seq_lens, block_size: int, kv_heads: int, head_dim: int,
+                    elem_bytes: int) -> int:
+    """K+V bytes of the distinct live (physical block, slot) positions the
+    tables reach: a block shared by several tables counts once, filled as far
+    as its fullest reader."""
+    fill: dict[int, int] = {}
+    for s, n in enumerate(np.asarray(seq_lens)):
+        n = int(n)
+        for j in range(_ceil_div(n, block_size)):
+            b = int(block_tables[s, j])
+            fill[b] = max(fill.get(b, 0), min(block_size, n - j * block_size))
+    return int(sum(fill.values())) * 2 * kv_heads * head_dim * elem_bytes
+
+
 def _fill_sequence(rng, k_cache, v_cache, blocks, live_tokens: int, dtype: str):
     """Random K/V in the first ``live_tokens`` slots of ``blocks`` (in order),
     NaN in the remaining slots of the last block."""

@@ -217,3 +217,62 @@ def test_swap_host_validation(built_lib):
     assert call(hkv=1, bs=1, d=3, dt=1) == 2        # 6-byte blocks
     assert call(n=0) == 0
     assert call() == 1                              # addresses no kernel can reach
+
+
+def test_shared_prefix_host_validation(built_lib):
+    """pa_decode_shared_prefix: group arrays, shapes and scale are checked
+    on the host before any launch; the workspace size follows the plan."""
+    lib = ctypes.CDLL(built_lib)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    fake = vp(4096)  # never dereferenced: every call below returns before a launch
+    fn = lib.pa_decode_shared_prefix
+    fn.restype = ctypes.c_int32
+    ws = lib.pa_decode_shared_prefix_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    base = dict(B=216, hq=64, hkv=8, d=128, bs=16, maxlen=2400, maxblk=150, nb=20000,
+                scale=0.088, starts=[0, 216], blocks=[125], ppart=512, part=0, dt=1,
+                ws_bytes=1 << 30, out=fake, q=fake)
+
+    def arrays(a):
+        n = len(a["blocks"])
+        return (i32 * len(a["starts"]))(*a["starts"]), (i32 * max(n, 1))(*(a["blocks"] or [0])), n
+
+    def call(**kw):
+        a = dict(base, **kw)
+        gs, gb, n = arrays(a)
+        return fn(a["out"], a["q"], fake, fake, fake, i32(a["maxblk"]), fake, i32(a["maxlen"]),
+                  i32(a["B"]), i32(a["hq"]), i32(a["hkv"]), i32(a["d"]), i32(a["bs"]),
+                  i32(a["nb"]), ctypes.c_float(a["scale"]), gs, gb, i32(n), i32(a["ppart"]),
+                  i32(a["part"]), fake, ctypes.c_size_t(a["ws_bytes"]), i32(a["dt"]), None)
+
+    def wsize(**kw):
+        a = dict(base, **kw)
+        gs, gb, n = arrays(a)
+        return ws(i32(a["B"]), i32(a["hq"]), i32(a["hkv"]), i32(a["d"]), i32(a["bs"]),
+                  i32(a["maxlen"]), i32(a["maxblk"]), gs, gb, i32(n), i32(a["ppart"]),
+                  i32(a["part"]), i32(a["dt"]))
+
+    INVALID, UNSUPPORTED = 1, 2
+    # 216 rows x 64 heads x (4 prefix partitions of 512 + 1 tail partition) x (128 + 2) fp32
+    assert wsize() == 216 * 64 * 5 * 130 * 4
+    assert wsize(ppart=100) == 216 * 64 * (16 + 1) * 130 * 4     # 100 -> 128 keys: 16 partitions
+    assert wsize(starts=[0, 216, 216], blocks=[125, 0]) == wsize()
+    assert wsize(starts=[3], blocks=[]) == 0                      # nothing shared, one partition
+    assert call(starts=[0, 217]) == INVALID                       # past the batch
+    assert call(starts=[-1, 216]) == INVALID
+    assert call(starts=[0, 100, 50], blocks=[125, 125]) == INVALID  # decreasing
+    assert call(blocks=[151]) == INVALID                          # more than the table holds
+    assert call(blocks=[-1]) == INVALID
+    assert call(maxlen=1999) == INVALID                           # prefix beyond max_seq_len
+    assert call(scale=0.0) == INVALID                             # prefix kernel needs scale > 0
+    assert call(scale=float("nan")) == INVALID
+    assert call(ppart=-1) == INVALID
+    assert call(ws_bytes=wsize() - 1) == INVALID
+    assert call(out=vp(4100)) == INVALID                          # not 16-byte aligned
+    assert call(starts=list(range(34)), blocks=[1] * 33) == UNSUPPORTED  # over 32 groups
+    assert call(dt=0) == UNSUPPORTED                              # fp32: no matrix-core path
+    assert call(hq=24, hkv=8) == UNSUPPORTED                      # group of 3
+    assert call(hq=64, hkv=2) == UNSUPPORTED                      # group of 32
+    assert call(d=96) == UNSUPPORTED
+    assert call(bs=8, maxblk=300, blocks=[250]) == UNSUPPORTED    # block below a 16-token tile
+    assert call(B=0, starts=[0, 0]) == 0                          # empty batch: nothing launched

@@ -139,3 +139,16 @@ def test_prefill_flops_counts_causal_pairs():
     lens, nq = [5, 9, 1], [5, 3, 1]
     pairs = sum(p + 1 for n, c in zip(lens, nq) for p in range(n - c, n))
     assert W.prefill_flops(lens, nq, num_heads=4, head_dim=8) == 4 * 8 * 4 * pairs
+
+
+def test_unique_kv_bytes_counts_shared_blocks_once():
+    bt = np.array([[3, 4, 0], [3, 5, 0], [6, 0, 0]], dtype=np.int32)
+    # b = 4; seqs share block 3 (full); block 4 holds 2 live slots, 5 holds 3, 6 holds 1
+    lens = np.array([6, 7, 1], dtype=np.int32)
+    per_token = 2 * 2 * 8 * 2                    # K+V, 2 KV heads, D = 8, bf16
+    assert W.unique_kv_bytes(bt, lens, 4, 2, 8, 2) == (4 + 2 + 3 + 1) * per_token
+    assert W.decode_kv_bytes(lens, 2, 8, 2) == 14 * per_token
+    w = W.tiny()
+    assert W.unique_kv_bytes(w.block_tables, w.seq_lens, w.block_size, w.kv_heads, w.head_dim,
+                             w.elem_bytes) == W.decode_kv_bytes(w.seq_lens, w.kv_heads,
+                                                                w.head_dim, w.elem_bytes)

@@ -189,11 +189,13 @@ Residency residency(const void* ptr, const void** kernel_ptr) {
 
 // Shared-prefix decode plan: the tail decode's plan on the matrix-core kernel
 // (partitions over the positions after the prefix) plus the prefix
-// partitions.  The prefix keys are split until the prefix kernel offers about
-// two work-groups per compute unit (kPrefixWgsPerCu); prefix_partition_size
+// partitions.  The prefix keys are split until the prefix work-groups fill
+// about one of the two work-group slots of every compute unit
+// (kPrefixWgsPerCu): they are dispatched first and run longest, and the tail
+// work-groups stream through the other slot meanwhile.  prefix_partition_size
 // > 0 fixes the split instead.  Groups with no member or no shared block
 // share nothing.
-constexpr int32_t kPrefixWgsPerCu = 2;
+constexpr int32_t kPrefixWgsPerCu = 1;
 static_assert(pa::kMaxPrefixGroups == PA_MAX_PREFIX_GROUPS, "group limit");
 
 pa_status shared_prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads,
@@ -555,8 +557,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
   p.num_layers = 1;
   p.prefix = pg;
   const hipStream_t s = (hipStream_t)stream;
-  if (pa::launch_prefix_attend(p, head_dim, s) != hipSuccess) return PA_ERR_HIP;
-  if (pa::launch_decode_mfma(p, head_dim, s) != hipSuccess) return PA_ERR_HIP;
+  if (pa::launch_shared_prefix(p, head_dim, s) != hipSuccess) return PA_ERR_HIP;
   return from_hip(pa::launch_prefix_merge(p, head_dim, s));
 }
 

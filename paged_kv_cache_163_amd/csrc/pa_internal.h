@@ -245,10 +245,11 @@ hipError_t launch_decode_reduce(const DecodeParams& p, bool is_bf16, int head_di
                                 hipStream_t stream);
 
 // Shared-prefix decode, bf16, head_dim in {64, 128}, group a power of two
-// <= 16: attention of every group member's query over the group's shared
-// keys (grid: p.prefix.wg_start[num_groups] work-groups), partials to the
-// workspace.
-hipError_t launch_prefix_attend(const DecodeParams& p, int head_dim, hipStream_t stream);
+// <= 16, block_size >= 16: one launch of the prefix attention (every group
+// member's query over the group's shared keys; p.prefix.wg_start[num_groups]
+// work-groups) and the tail decode (num_partitions - prefix.parts partitions
+// per sequence and KV head), partials to the workspace.
+hipError_t launch_shared_prefix(const DecodeParams& p, int head_dim, hipStream_t stream);
 // Merge of prefix and tail partials, one work-group per (sequence, KV head);
 // also checks that members' tables start with their leader's blocks.
 hipError_t launch_prefix_merge(const DecodeParams& p, int head_dim, hipStream_t stream);

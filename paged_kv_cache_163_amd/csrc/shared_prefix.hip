@@ -1,0 +1,273 @@
+// Shared-prefix decode: groups of sequences whose block tables start with the
+// same physical blocks (one prefix, refcounted, N tables pointing at it: "How
+// PagedAttention works", section "A strong answer"; lihaoran.work explainer,
+// section "Shared prefixes need matching computation").
+//
+// Plain decode reads a shared prefix block once per sequence.  Here the
+// decode queries of all members of a group attend the shared keys together:
+// rows are (member, query head) pairs of one KV head, 128 per work-group, over
+// one partition of the prefix keys, on the row-tile engine of row_tiles.h, so
+// each shared K/V tile is fetched once per work-group and the contraction runs
+// on the matrix cores at 128 rows instead of G.  No causal limit applies: a
+// decode query sits after its whole prefix.  Each member's positions after the
+// prefix go through the decode work-group (decode_mfma.h, tail mode).  Both
+// leave softmax partials (unnormalised O, max m, sum l) in the workspace, and
+// prefix_merge_kernel combines them with the cross-partition formula of
+// decode_reduce.hip.
+//
+// The prefix and tail work-groups share one launch, prefix first.  The host
+// splits the prefix keys so that the prefix work-groups take about one of the
+// two work-group slots of each compute unit; they run longest, and the short,
+// latency-bound tail work-groups stream through the other slot meanwhile
+// (measured on the shared-prefix workload: 78 us for the call against 94 us
+// with the prefix and the tails in two launches, and 98 us with the two kinds
+// alternating in one launch).
+#include "decode_mfma.h"
+#include "row_tiles.h"
+
+namespace pa {
+namespace {
+
+using namespace mfma;
+
+// Prefix part: work-group x of the prefix attention.  Group g owns prefix
+// work-groups wg_start[g] ..; inside it, all member tiles of one (partition,
+// KV head) pair run on one XCD (x % 8 is kept from the launch index), so the
+// pair's K/V tiles stay in that XCD's L2.
+template <int D>
+__device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x) {
+  constexpr int kVd = D / 16;
+  const PrefixGroups& pg = p.prefix;
+  int grp = 0;
+  for (int i = 1; i < pg.num_groups; ++i)
+    if (x >= pg.wg_start[i]) grp = i;
+  const int local = x - pg.wg_start[grp];
+  const int first = pg.start[grp];
+  const int members = pg.start[grp + 1] - first;
+  const int tokens = pg.tokens[grp];
+  const int G = p.group;
+  const int tiles = ceil_div_i(members * G, kPrefillRows);
+  const int combos = p.kv_heads * ceil_div_i(tokens, pg.partition);
+  const int slot = local >> 3;
+  const int combo = (slot / tiles) * 8 + (local & 7);
+  if (combo >= combos) return;
+  const int tile = slot - (slot / tiles) * tiles;
+  const int head = combo % p.kv_heads;
+  const int kp = combo / p.kv_heads;
+  const int kstart = kp * pg.partition;
+  const int kend_wg = min(tokens, kstart + pg.partition);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int m0 = tile * (kPrefillRows / G);  // first member of the work-group
+  const int wrow0 = wave * kWaveRows;
+  const bool wave_rows = m0 + wrow0 / G < members;
+  // every row sees every key of the partition: the mask only cuts the last
+  // step at kend_wg
+  const int kend = wave_rows ? kend_wg : kstart;
+  const int kfull = kend_wg - 1;
+
+  u32x4 qb[kRowTiles][D / 32];
+  int lim[kRowTiles];
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+    const int row = wrow0 + 16 * nr + r16;
+    const int mi = m0 + row / G;
+    const int g = row - (row / G) * G;
+    const bool valid = mi < members;
+    lim[nr] = kend_wg - 1;
+    const char* qrow = (const char*)p.q +
+                       (((int64_t)(first + mi) * p.num_heads + (int64_t)head * G + g) * D) * 2 +
+                       q4 * 16;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+      qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  SeqView c;
+  const int64_t head_stride = (int64_t)p.block_size * D * 2;
+  c.kbase = (const char*)p.k_cache + (int64_t)head * head_stride;
+  c.vbase = (const char*)p.v_cache + (int64_t)head * head_stride;
+  c.table = p.block_tables + (int64_t)first * p.max_blocks_per_seq;  // the leader's row
+  c.block_stride = (int64_t)p.kv_heads * head_stride;
+  c.nblocks_valid = tokens >> p.block_shift;
+  c.num_blocks = p.num_blocks;
+  c.block_shift = p.block_shift;
+  c.bmask = p.block_size - 1;
+
+  PfAcc<D> a[kRowTiles];
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+#pragma unroll
+    for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    a[nr].l = f32x4{0.f, 0.f, 0.f, 0.f};
+    a[nr].m = -INFINITY;
+  }
+  bool bad = false;
+  __shared__ __attribute__((aligned(16))) unsigned char sm_kv[2][2 * 32 * kKvStride<D>];
+  attend_keys<D>(a, c, qb, lim, kstart, kend_wg, kend, kfull, p.scale_log2, bad, sm_kv, tid,
+                 r16, q4);
+  if (!wave_rows) return;
+
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+    const int row = wrow0 + 16 * nr + r16;
+    const int mi = m0 + row / G;
+    const int g = row - (row / G) * G;
+    if (mi >= members) continue;
+    const int64_t wslot =
+        ((int64_t)(first + mi) * p.num_heads + (int64_t)head * G + g) * p.num_partitions + kp;
+    // o[jt][rr] is head dim 16 jt + 4 q4 + rr of the lane's row
+    float* orow = p.ws_o + wslot * D + 4 * q4;
+#pragma unroll
+    for (int jt = 0; jt < kVd; ++jt) *(f32x4*)(orow + 16 * jt) = a[nr].o[jt];
+    if (q4 == 0) {
+      p.ws_ml[wslot * 2 + 0] = a[nr].m;
+      p.ws_ml[wslot * 2 + 1] = bad ? __builtin_nanf("") : a[nr].l[0];  // a bad table: NaN rows
+    }
+  }
+}
+
+
+// Two resident work-groups per compute unit (both kinds fit 256 registers
+// per lane; without the bound the allocator spends AGPRs and halves that).
+template <int D>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void shared_prefix_kernel(DecodeParams p, int prefix_blocks, int tail_blocks, int tail_wgs,
+                          bool interleave) {
+  const int x = blockIdx.x;
+  const int blk = x >> 3;
+  int kind, idx;
+  if (interleave) {
+    const int both = min(prefix_blocks, tail_blocks);
+    if (blk < 2 * both) {
+      kind = blk & 1;
+      idx = (blk >> 1) * 8 + (x & 7);
+    } else {
+      kind = prefix_blocks > tail_blocks ? 0 : 1;
+      idx = (blk - both) * 8 + (x & 7);
+    }
+  } else {  // prefix blocks first
+    kind = blk < prefix_blocks ? 0 : 1;
+    idx = (kind == 0 ? blk : blk - prefix_blocks) * 8 + (x & 7);
+  }
+  if (kind == 0)
+    prefix_wg<D>(p, idx);
+  else if (idx < tail_wgs)
+    decode_wg<D, kModeTail>(p, idx);
+}
+
+// Merge of each row's prefix partials (slots [0, kp), one per prefix
+// partition) and tail partials (slots prefix.parts + [0, tp)):
+//     out = sum_q w_q o_q / sum_q w_q l_q,  w_q = exp2(m_q - max_q m_q).
+// One 256-thread work-group per (sequence, KV head); a thread owns four
+// consecutive output elements of one query head and reads that head's
+// partials itself, all loads of a round issued together.  A member whose
+// table does not start with its leader's prefix blocks, or whose length stops
+// inside the prefix, gets a NaN row (the prefix partials are not its keys).
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(DecodeParams p) {
+  const int head = blockIdx.x % p.kv_heads;
+  const int seq = blockIdx.x / p.kv_heads;
+  const int len = p.seq_lens[seq];
+  if (!seq_len_ok(p, len)) return;  // the tail work-group already wrote NaN
+  const int grp = shared_prefix_group(p.prefix, seq);
+  const int pfx = grp >= 0 ? p.prefix.tokens[grp] : 0;
+  const int kp = pfx > 0 ? ceil_div_i(pfx, p.prefix.partition) : 0;
+  const int tp = len > pfx ? ceil_div_i(len - pfx, p.partition_size) : 0;
+  if (pfx == 0 && tp <= 1) return;  // the tail work-group wrote the row itself
+  const int tid = threadIdx.x;
+  bool diff = pfx > 0 && len < pfx;
+  if (pfx > 0) {
+    const int32_t* mine = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
+    const int32_t* lead = p.block_tables + (int64_t)p.prefix.start[grp] * p.max_blocks_per_seq;
+    for (int j = tid; j < (pfx >> p.block_shift); j += kMergeThreads) diff |= mine[j] != lead[j];
+  }
+  const bool bad = __syncthreads_or(diff);
+  const int G = p.group;
+  const int n = kp + tp;
+  const int64_t row0 = (int64_t)seq * p.num_heads + (int64_t)head * G;
+  uint16_t* out = (uint16_t*)p.out;
+  for (int i = 4 * tid; i < G * D; i += 4 * kMergeThreads) {
+    const int g = i / D;
+    const int d = i - g * D;
+    const float* ml = p.ws_ml + (row0 + g) * p.num_partitions * 2;
+    const float* o = p.ws_o + (row0 + g) * p.num_partitions * D + d;
+    float mx = -INFINITY;
+#pragma unroll 8
+    for (int q = 0; q < n; ++q) mx = fmaxf(mx, ml[2 * (q < kp ? q : p.prefix.parts + q - kp)]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < n; ++q) {
+      const int slot = q < kp ? q : p.prefix.parts + (q - kp);
+      const float w = exp2f(ml[2 * slot] - mx);
+      l += w * ml[2 * slot + 1];
+      acc += w * *(const f32x4*)(o + (int64_t)slot * D);
+    }
+    const float inv = bad ? __builtin_nanf("") : 1.0f / l;
+    *(u32x2*)(out + (row0 + g) * D + d) =
+        u32x2{pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
+  }
+}
+
+// Launch layout (tuning knob): 0 = the prefix work-groups, then the tails in
+// a launch of the decode kernel; 1 = one launch, kinds alternating in blocks
+// of eight work-groups (one per XCD); 2 = one launch, prefix blocks first.
+#ifndef PA_SHARED_PREFIX_LAUNCH
+#define PA_SHARED_PREFIX_LAUNCH 2
+#endif
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void tail_decode_kernel(DecodeParams p) {
+  decode_wg<D, kModeTail>(p, blockIdx.x);
+}
+
+template <int D>
+hipError_t launch_sp(const DecodeParams& p, hipStream_t stream) {
+  const int64_t prefix_wgs = p.prefix.wg_start[p.prefix.num_groups];  // a multiple of 8
+  const int64_t tail_wgs = (int64_t)(p.num_partitions - p.prefix.parts) * p.num_seqs * p.kv_heads;
+  const int64_t pb = (prefix_wgs + 7) / 8, tb = (tail_wgs + 7) / 8;
+  if ((pb + tb) * 8 > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 block(kPfWaves * 64);
+  if (PA_SHARED_PREFIX_LAUNCH == 0) {
+    if (pb > 0)
+      shared_prefix_kernel<D><<<dim3((unsigned)(pb * 8)), block, 0, stream>>>(p, (int)pb, 0, 0,
+                                                                               false);
+    if (tail_wgs > 0) tail_decode_kernel<D><<<dim3((unsigned)tail_wgs), block, 0, stream>>>(p);
+  } else if (PA_SHARED_PREFIX_LAUNCH == 1) {
+    shared_prefix_kernel<D><<<dim3((unsigned)((pb + tb) * 8)), block, 0, stream>>>(
+        p, (int)pb, (int)tb, (int)tail_wgs, true);
+  } else {
+    shared_prefix_kernel<D><<<dim3((unsigned)((pb + tb) * 8)), block, 0, stream>>>(
+        p, (int)pb, (int)tb, (int)tail_wgs, false);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_shared_prefix(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) return launch_sp<128>(p, stream);
+  if (head_dim == 64) return launch_sp<64>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefix_merge(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  if (p.group > 16 || head_dim % 4 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((int64_t)p.num_seqs * p.kv_heads));
+  if (head_dim == 64)
+    prefix_merge_kernel<64><<<grid, kMergeThreads, 0, stream>>>(p);
+  else if (head_dim == 128)
+    prefix_merge_kernel<128><<<grid, kMergeThreads, 0, stream>>>(p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pa

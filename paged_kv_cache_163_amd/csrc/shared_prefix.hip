@@ -165,10 +165,18 @@ void shared_prefix_kernel(DecodeParams p, int prefix_blocks, int tail_blocks, in
 //     out = sum_q w_q o_q / sum_q w_q l_q,  w_q = exp2(m_q - max_q m_q).
 // One 256-thread work-group per (sequence, KV head); a thread owns four
 // consecutive output elements of one query head and reads that head's
-// partials itself, all loads of a round issued together.  A member whose
-// table does not start with its leader's prefix blocks, or whose length stops
-// inside the prefix, gets a NaN row (the prefix partials are not its keys).
+// partials itself.  Up to kMergeRegs partials are loaded into registers in
+// one round together with the table check, so the work-group waits on two
+// memory latencies (its length, then everything else); longer lists loop.  A
+// member whose table does not start with its leader's prefix blocks, or whose
+// length stops inside the prefix, gets a NaN row (the prefix partials are not
+// its keys).
 constexpr int kMergeThreads = 256;
+constexpr int kMergeRegs = 8;
+
+__device__ inline int merge_slot(const DecodeParams& p, int kp, int q) {
+  return q < kp ? q : p.prefix.parts + (q - kp);
+}
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(DecodeParams p) {
@@ -182,6 +190,29 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(DecodeParam
   const int tp = len > pfx ? ceil_div_i(len - pfx, p.partition_size) : 0;
   if (pfx == 0 && tp <= 1) return;  // the tail work-group wrote the row itself
   const int tid = threadIdx.x;
+  const int G = p.group;
+  const int n = kp + tp;
+  const int64_t row0 = (int64_t)seq * p.num_heads + (int64_t)head * G;
+  uint16_t* out = (uint16_t*)p.out;
+  // the first item of this thread, loaded before the table check
+  const int i0 = 4 * tid;
+  const bool has0 = i0 < G * D;
+  const int g0 = i0 / D;
+  float m0[kMergeRegs], l0[kMergeRegs];
+  f32x4 o0[kMergeRegs];
+  if (has0 && n <= kMergeRegs) {
+    const float* ml = p.ws_ml + (row0 + g0) * p.num_partitions * 2;
+    const float* o = p.ws_o + (row0 + g0) * p.num_partitions * D + (i0 - g0 * D);
+#pragma unroll
+    for (int q = 0; q < kMergeRegs; ++q) {
+      if (q < n) {
+        const int slot = merge_slot(p, kp, q);
+        m0[q] = ml[2 * slot];
+        l0[q] = ml[2 * slot + 1];
+        o0[q] = *(const f32x4*)(o + (int64_t)slot * D);
+      }
+    }
+  }
   bool diff = pfx > 0 && len < pfx;
   if (pfx > 0) {
     const int32_t* mine = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
@@ -189,26 +220,36 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(DecodeParam
     for (int j = tid; j < (pfx >> p.block_shift); j += kMergeThreads) diff |= mine[j] != lead[j];
   }
   const bool bad = __syncthreads_or(diff);
-  const int G = p.group;
-  const int n = kp + tp;
-  const int64_t row0 = (int64_t)seq * p.num_heads + (int64_t)head * G;
-  uint16_t* out = (uint16_t*)p.out;
-  for (int i = 4 * tid; i < G * D; i += 4 * kMergeThreads) {
+  for (int i = i0; i < G * D; i += 4 * kMergeThreads) {
     const int g = i / D;
     const int d = i - g * D;
-    const float* ml = p.ws_ml + (row0 + g) * p.num_partitions * 2;
-    const float* o = p.ws_o + (row0 + g) * p.num_partitions * D + d;
-    float mx = -INFINITY;
-#pragma unroll 8
-    for (int q = 0; q < n; ++q) mx = fmaxf(mx, ml[2 * (q < kp ? q : p.prefix.parts + q - kp)]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float l = 0.f;
-#pragma unroll 8
-    for (int q = 0; q < n; ++q) {
-      const int slot = q < kp ? q : p.prefix.parts + (q - kp);
-      const float w = exp2f(ml[2 * slot] - mx);
-      l += w * ml[2 * slot + 1];
-      acc += w * *(const f32x4*)(o + (int64_t)slot * D);
+    if (i == i0 && n <= kMergeRegs) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kMergeRegs; ++q)
+        if (q < n) mx = fmaxf(mx, m0[q]);
+#pragma unroll
+      for (int q = 0; q < kMergeRegs; ++q) {
+        if (q < n) {
+          const float w = exp2f(m0[q] - mx);
+          l += w * l0[q];
+          acc += w * o0[q];
+        }
+      }
+    } else {
+      const float* ml = p.ws_ml + (row0 + g) * p.num_partitions * 2;
+      const float* o = p.ws_o + (row0 + g) * p.num_partitions * D + d;
+      float mx = -INFINITY;
+      for (int q = 0; q < n; ++q) mx = fmaxf(mx, ml[2 * merge_slot(p, kp, q)]);
+#pragma unroll 4
+      for (int q = 0; q < n; ++q) {
+        const int slot = merge_slot(p, kp, q);
+        const float w = exp2f(ml[2 * slot] - mx);
+        l += w * ml[2 * slot + 1];
+        acc += w * *(const f32x4*)(o + (int64_t)slot * D);
+      }
     }
     const float inv = bad ? __builtin_nanf("") : 1.0f / l;
     *(u32x2*)(out + (row0 + g) * D + d) =

@@ -39,13 +39,14 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/sec, 1 GPU"
 # Sources each profiled kernel is built from: a stored counter record is used
 # only while their hash still matches.
+_CSRC = "paged_kv_cache_163_amd/csrc/"
 KERNEL_SOURCES = {
-    "decode_mfma_kernel": ["paged_kv_cache_163_amd/csrc/decode_mfma.hip",
-                           "paged_kv_cache_163_amd/csrc/mfma_step.h",
-                           "paged_kv_cache_163_amd/csrc/pa_internal.h"],
-    "prefill_mfma_kernel": ["paged_kv_cache_163_amd/csrc/prefill_mfma.hip",
-                            "paged_kv_cache_163_amd/csrc/mfma_step.h",
-                            "paged_kv_cache_163_amd/csrc/pa_internal.h"],
+    "decode_mfma_kernel": [_CSRC + f for f in ("decode_mfma.hip", "decode_mfma.h", "mfma_step.h",
+                                               "pa_internal.h")],
+    "prefill_mfma_kernel": [_CSRC + f for f in ("prefill_mfma.hip", "row_tiles.h", "mfma_step.h",
+                                                "pa_internal.h")],
+    "shared_prefix_kernel": [_CSRC + f for f in ("shared_prefix.hip", "decode_mfma.h",
+                                                 "row_tiles.h", "mfma_step.h", "pa_internal.h")],
 }
 
 
@@ -587,13 +588,17 @@ def main():
     kernel_name = f"decode_{plan.kernel}_kernel" + (" (fused append)" if fused else "")
     split_reduce = plan.kernel != "stream" and nparts > 1
     if shared:
-        kernel_name = "prefix_attend_kernel + decode_mfma_kernel (tails) + prefix_merge_kernel"
+        kernel_name = "shared_prefix_kernel (prefix + tails) + prefix_merge_kernel"
         split_reduce = False
     dec_avg = float(dec_ms.mean())
     achieved = unique_bytes / (dec_avg * 1e-3) / 1e9
     # the stored counter record is for the plain decode kernel at the default plan
-    plain = args.partition == 0 and args.kernel == "auto" and not fused and not shared
-    traffic = traffic_entry(w.name) if plain else None
+    plain = args.partition == 0 and args.kernel == "auto" and not fused
+    traffic = None
+    if plain and shared and args.prefix_partition == 0:
+        traffic = traffic_entry(w.name, "shared_prefix_kernel")
+    elif plain and not shared:
+        traffic = traffic_entry(w.name)
 
     line = {
         "metric": METRIC,

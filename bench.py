@@ -151,17 +151,22 @@ class HipTimer:
         self._events = []
 
 
+def blas_threads() -> int:
+    """Threads numpy's BLAS may use for the oracle's products (1 if unknown)."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return int(max([i.get("num_threads", 1) for i in blas] or [1]))
+    except Exception:  # threadpoolctl missing: numpy BLAS thread count unknown
+        return 1
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle, as it stands, on whole-batch sequences until ~seconds pass."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max([i.get("num_threads", 1) for i in blas] or [1])
-    except Exception:  # threadpoolctl missing: numpy BLAS thread count unknown
-        threads = 1
+    threads = blas_threads()
     order = np.random.default_rng(123).permutation(w.num_seqs)
     done, kv_bytes = 0, 0
     t0 = time.perf_counter()
@@ -210,7 +215,7 @@ def prefill_cpu_baseline(w, seconds: float):
     return {
         "value": round(flops / dt / 1e12, 9),
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": blas_threads(),
         "kind": "oracle",
         "sample": (f"{done} query rows of the {w.name} batch (random order, seed 123, each "
                    f"with its sequence's gather), {dt:.1f} s single process, numpy float64; "

@@ -1,11 +1,13 @@
 """Summaries of rocprofv3 runs of bench.py for the profiles/ directory.
 
     python -m paged_kv_cache_163_amd.profiling stats   TRACE_DIR  OUT.md  "COMMAND"
+    python -m paged_kv_cache_163_amd.profiling counters PMC_DIR KERNEL WORKLOAD OUT.md "COMMAND"
     python -m paged_kv_cache_163_amd.profiling traffic FETCH_DIR WRITE_DIR CAL_FETCH_DIR \
         CAL_WRITE_DIR KERNEL WORKLOAD OUT.json OUT.md "COMMANDS"
 
 ``stats`` condenses a ``rocprofv3 --kernel-trace --stats`` run (the
-``*_kernel_stats.csv`` it writes) into a markdown table.
+``*_kernel_stats.csv`` it writes) into a markdown table; ``counters`` does the
+same for the per-dispatch values of one kernel in a ``--pmc`` run.
 
 ``traffic`` turns two ``rocprofv3 --pmc`` runs of the benchmark (FETCH_SIZE,
 then WRITE_SIZE, in KiB per dispatch) into HBM bytes per launch of KERNEL.
@@ -77,7 +79,30 @@ def traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel):
     }
 
 
+def counters_md(run_dir: str, kernel: str, workload: str, command: str) -> str:
+    """Per-dispatch counter values of KERNEL (median over its dispatches, in
+    millions) from a ``rocprofv3 --pmc`` run."""
+    rows = [r for r in _csv(run_dir, "counter_collection.csv")
+            if r["Kernel_Name"].startswith(kernel)]
+    by: dict[str, dict[str, float]] = {}
+    for r in rows:  # one row per (dispatch, counter)
+        d = by.setdefault(r["Counter_Name"], {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    lines = [f"Command: `{command}`", "",
+             f"Kernel `{kernel}`, workload `{workload}`; counter sums per dispatch (median over "
+             f"{len(next(iter(by.values()), {}))} dispatches), millions.", "",
+             "| counter | per dispatch (M) |", "|---|---|"]
+    for name in sorted(by):
+        lines.append(f"| {name} | {statistics.median(by[name].values()) / 1e6:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv):
+    if argv[0] == "counters":
+        run_dir, kernel, workload, out_md, command = argv[1:6]
+        with open(out_md, "w") as f:
+            f.write(counters_md(run_dir, kernel, workload, command))
+        return
     if argv[0] == "stats":
         trace_dir, out_md, command = argv[1:4]
         with open(out_md, "w") as f:

@@ -21,7 +21,8 @@
 // latency-bound tail work-groups stream through the other slot meanwhile
 // (measured on the shared-prefix workload: 78 us for the call against 94 us
 // with the prefix and the tails in two launches, and 98 us with the two kinds
-// alternating in one launch).
+// alternating in one launch; the layouts were compared on one box in one
+// run).
 #include "decode_mfma.h"
 #include "row_tiles.h"
 
@@ -134,30 +135,16 @@ __device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x) {
 
 // Two resident work-groups per compute unit (both kinds fit 256 registers
 // per lane; without the bound the allocator spends AGPRs and halves that).
+// Work-group x: the prefix attention's work-group x while x < prefix_wgs (a
+// multiple of 8, so x % 8 still names the XCD), then the tails.
 template <int D>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void shared_prefix_kernel(DecodeParams p, int prefix_blocks, int tail_blocks, int tail_wgs,
-                          bool interleave) {
+void shared_prefix_kernel(DecodeParams p, int prefix_wgs) {
   const int x = blockIdx.x;
-  const int blk = x >> 3;
-  int kind, idx;
-  if (interleave) {
-    const int both = min(prefix_blocks, tail_blocks);
-    if (blk < 2 * both) {
-      kind = blk & 1;
-      idx = (blk >> 1) * 8 + (x & 7);
-    } else {
-      kind = prefix_blocks > tail_blocks ? 0 : 1;
-      idx = (blk - both) * 8 + (x & 7);
-    }
-  } else {  // prefix blocks first
-    kind = blk < prefix_blocks ? 0 : 1;
-    idx = (kind == 0 ? blk : blk - prefix_blocks) * 8 + (x & 7);
-  }
-  if (kind == 0)
-    prefix_wg<D>(p, idx);
-  else if (idx < tail_wgs)
-    decode_wg<D, kModeTail>(p, idx);
+  if (x < prefix_wgs)
+    prefix_wg<D>(p, x);
+  else
+    decode_wg<D, kModeTail>(p, x - prefix_wgs);
 }
 
 // Merge of each row's prefix partials (slots [0, kp), one per prefix
@@ -257,46 +244,21 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(DecodeParam
   }
 }
 
-// Launch layout (tuning knob): 0 = the prefix work-groups, then the tails in
-// a launch of the decode kernel; 1 = one launch, kinds alternating in blocks
-// of eight work-groups (one per XCD); 2 = one launch, prefix blocks first.
-#ifndef PA_SHARED_PREFIX_LAUNCH
-#define PA_SHARED_PREFIX_LAUNCH 2
-#endif
-
-template <int D>
-__global__ __launch_bounds__(kWaves * 64) void tail_decode_kernel(DecodeParams p) {
-  decode_wg<D, kModeTail>(p, blockIdx.x);
-}
-
-template <int D>
-hipError_t launch_sp(const DecodeParams& p, hipStream_t stream) {
-  const int64_t prefix_wgs = p.prefix.wg_start[p.prefix.num_groups];  // a multiple of 8
-  const int64_t tail_wgs = (int64_t)(p.num_partitions - p.prefix.parts) * p.num_seqs * p.kv_heads;
-  const int64_t pb = (prefix_wgs + 7) / 8, tb = (tail_wgs + 7) / 8;
-  if ((pb + tb) * 8 > INT32_MAX) return hipErrorInvalidValue;
-  const dim3 block(kPfWaves * 64);
-  if (PA_SHARED_PREFIX_LAUNCH == 0) {
-    if (pb > 0)
-      shared_prefix_kernel<D><<<dim3((unsigned)(pb * 8)), block, 0, stream>>>(p, (int)pb, 0, 0,
-                                                                               false);
-    if (tail_wgs > 0) tail_decode_kernel<D><<<dim3((unsigned)tail_wgs), block, 0, stream>>>(p);
-  } else if (PA_SHARED_PREFIX_LAUNCH == 1) {
-    shared_prefix_kernel<D><<<dim3((unsigned)((pb + tb) * 8)), block, 0, stream>>>(
-        p, (int)pb, (int)tb, (int)tail_wgs, true);
-  } else {
-    shared_prefix_kernel<D><<<dim3((unsigned)((pb + tb) * 8)), block, 0, stream>>>(
-        p, (int)pb, (int)tb, (int)tail_wgs, false);
-  }
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_shared_prefix(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return launch_sp<128>(p, stream);
-  if (head_dim == 64) return launch_sp<64>(p, stream);
-  return hipErrorInvalidValue;
+  const int64_t prefix_wgs = p.prefix.wg_start[p.prefix.num_groups];  // a multiple of 8
+  const int64_t tail_wgs = (int64_t)(p.num_partitions - p.prefix.parts) * p.num_seqs * p.kv_heads;
+  if (prefix_wgs + tail_wgs > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(prefix_wgs + tail_wgs));
+  const dim3 block(kPfWaves * 64);
+  if (head_dim == 128)
+    shared_prefix_kernel<128><<<grid, block, 0, stream>>>(p, (int)prefix_wgs);
+  else if (head_dim == 64)
+    shared_prefix_kernel<64><<<grid, block, 0, stream>>>(p, (int)prefix_wgs);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_prefix_merge(const DecodeParams& p, int head_dim, hipStream_t stream) {

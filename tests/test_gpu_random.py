@@ -174,3 +174,41 @@ def test_random_shared_prefix(pa, case):
     assert_close(oracle.to_f64(host(out)), ref, "bf16",
                  f"case {case}: D={head_dim} Hkv={kv_heads} G={group} b={block_size} "
                  f"groups={bounds} prefix={prefix} P={ppart}")
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_fused_append(pa, case):
+    """pa_decode_append: one new token per sequence (slot -1 for about one
+    sequence in five, whose length then stays put), appended and decoded in
+    one launch.  The cache must match the oracle's append bit for bit."""
+    rng = np.random.default_rng([20261202, 4, case])
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    head_dim = int(rng.choice([64, 128]))
+    kv_heads = int(rng.integers(1, 5))
+    group = int(rng.choice([1, 2, 4, 8] if dtype == "f32" else [1, 2, 4, 8, 16]))
+    block_size = int(rng.choice([1, 4, 16, 32] if dtype == "f32" else [16, 32, 64]))
+    pre = draw_lengths(rng, int(rng.integers(1, 25)), 1500)
+    nb = int(sum(-(-(int(n) + 1) // block_size) for n in pre)) + 8
+    w = W.build_private("random_fused", pre, dtype=dtype, num_heads=kv_heads * group,
+                        kv_heads=kv_heads, head_dim=head_dim, block_size=block_size,
+                        num_blocks=nb, append=True, seed=4000 + case)
+    k_new, v_new, slots = W.per_sequence_append(w)
+    skip = rng.random(len(pre)) < 0.2
+    slots[skip] = -1
+    lens = np.where(skip, w.pre_lens, w.seq_lens).astype(np.int32)
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    oracle.kv_append(kc, vc, k_new[~skip], v_new[~skip], slots[~skip], block_size)
+    ref = oracle.paged_decode(w.q, kc, vc, w.block_tables, lens, w.scale, block_size)
+    part = int(rng.choice([0, 0, 16, 32, 96, 512]))
+    kernels = ["valu"] if dtype == "f32" else ["mfma"] + (["valu"] if group <= 8 else [])
+    what = (f"case {case}: {dtype} D={head_dim} Hkv={kv_heads} G={group} b={block_size} "
+            f"B={len(pre)} P={part}")
+    for kernel in kernels:
+        k, v = dev(w.k_cache), dev(w.v_cache)
+        out = pa.decode_append(dev(w.q), k, v, dev(k_new), dev(v_new), dev(slots),
+                               dev(w.block_tables), dev(lens), w.scale,
+                               max_seq_len=int(lens.max()), partition_size=part, kernel=kernel)
+        torch.cuda.synchronize()
+        assert np.array_equal(raw(host(k)), raw(kc)) and np.array_equal(raw(host(v)), raw(vc)), \
+            f"{what} {kernel}: cache"
+        assert_close(oracle.to_f64(host(out)), ref, dtype, f"{what} {kernel}")

@@ -137,9 +137,9 @@ __device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_his
 // kModeLayered: one or more layers of a layered pool (layer = blockIdx.y).
 // kModeOrdered: a per-layer pool with the caller's longest-first order.
 // kModeTail: shared-prefix decode; each sequence's partitions start after
-// its group's shared prefix (prefix_attend covers the prefix), index order,
-// and every partial goes to the workspace unless the sequence has no prefix
-// and one partition.
+// its group's shared prefix (the prefix work-groups of shared_prefix.hip
+// cover the prefix), in index order, and every partial goes to the
+// workspace unless the sequence has no prefix and one partition.
 enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered, kModeTail };
 
 // The work of decode work-group `wg` (sequence, KV head, partition) in mode M.

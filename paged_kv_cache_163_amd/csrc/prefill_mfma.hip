@@ -125,7 +125,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     a[nr].m = -INFINITY;
   }
   bool bad = false;
-  // The key loop of attend_keys, written out.
+  // The key loop of attend_keys (row_tiles.h), written out in the kernel.
   __shared__ __attribute__((aligned(16))) unsigned char sm_kv[2][2 * 32 * kKvStride<D>];
   {
     const StagePlan<D> sp = stage_plan<D>(c, tid);

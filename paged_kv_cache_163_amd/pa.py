@@ -330,10 +330,18 @@ def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, scale, gro
     """
     gs, gb, n = _host_groups(group_start, group_prefix_blocks)
     dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k_cache and v_cache must share a dtype")
     B, hq, d = q.shape
-    nb, hkv, bs, _ = k_cache.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shape does not match q")
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must be [num_seqs]")
+    if out is not None and (out.shape != q.shape or out.dtype != q.dtype):
+        raise ValueError("out must match q")
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
     maxblk = int(block_tables.shape[1])

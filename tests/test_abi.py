@@ -276,3 +276,20 @@ def test_shared_prefix_host_validation(built_lib):
     assert call(d=96) == UNSUPPORTED
     assert call(bs=8, maxblk=300, blocks=[250]) == UNSUPPORTED    # block below a 16-token tile
     assert call(B=0, starts=[0, 0]) == 0                          # empty batch: nothing launched
+
+
+def test_header_is_c_and_the_library_links_from_c(built_lib, tmp_path):
+    """include/pa.h is plain C99 (extern "C" only under C++), and a C program
+    linked against libpa.so runs the host-side calls (tests/c/abi_from_c.c)."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(ROOT, "tests", "c", "abi_from_c.c")
+    exe = str(tmp_path / "abi_from_c")
+    libdir = os.path.dirname(built_lib)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), src, "-o", exe, "-L", libdir, "-lpa",
+                    f"-Wl,-rpath,{libdir}"], check=True, capture_output=True, text=True)
+    res = subprocess.run([exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr

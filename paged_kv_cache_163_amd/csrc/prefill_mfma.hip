@@ -151,21 +151,40 @@ void prefill_mfma_kernel(PrefillParams p) {
   }
   if (!wave_rows) return;
 
+  // The output rows go through LDS (the staging buffers, free since the key
+  // loop's last barrier): each wave writes its 32 normalised bf16 rows there
+  // and stores them back in whole 16-byte parts, so every store instruction
+  // writes full rows (contiguous for the G heads of one query) instead of a
+  // 32-byte piece of 16 rows.  A wave reads only its own rows, and one wave's
+  // LDS operations complete in order.
+  constexpr int kOutStride = D * 2 + 16;       // bytes per staged row (padded)
+  constexpr int kParts = D * 2 / 16;           // 16-byte parts per row
+  constexpr int kRowsPerStore = 64 / kParts;   // rows one store instruction covers
+  static_assert(kPfWaves * kWaveRows * kOutStride <= 2 * 2 * 32 * kKvStride<D>, "fits");
+  unsigned char* ow = &sm_kv[0][0] + wave * kWaveRows * kOutStride;
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr) {
-    const int row = wrow0 + 16 * nr + r16;
-    const int qi = i0 + row / G;
-    const int g = row - (row / G) * G;
-    if (qi >= nq) continue;
     const float inv = bad ? __builtin_nanf("") : 1.0f / a[nr].l[0];
     // o[jt][rr] is head dim 16 jt + 4 q4 + rr of the lane's row
-    uint16_t* orow = out + (int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D + 4 * q4;
+    unsigned char* lrow = ow + (16 * nr + r16) * kOutStride + 8 * q4;
 #pragma unroll
     for (int jt = 0; jt < kVd; ++jt) {
       const f32x4 o = a[nr].o[jt];
-      *(u32x2*)(orow + 16 * jt) = u32x2{pack_bf16(o[0] * inv, o[1] * inv),
+      *(u32x2*)(lrow + 32 * jt) = u32x2{pack_bf16(o[0] * inv, o[1] * inv),
                                         pack_bf16(o[2] * inv, o[3] * inv)};
     }
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int it = 0; it < kWaveRows / kRowsPerStore; ++it) {
+    const int lr = it * kRowsPerStore + lane / kParts;  // the wave's row 16 nr + r16
+    const int part = lane % kParts;
+    const int row = wrow0 + lr;
+    const int qi = i0 + row / G;
+    const int g = row - (row / G) * G;
+    const u32x4 v = *(const u32x4*)(ow + lr * kOutStride + 16 * part);
+    if (qi < nq)
+      *(u32x4*)(out + (int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D + 8 * part) = v;
   }
 }
 

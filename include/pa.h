@@ -14,8 +14,11 @@
  * Common conventions for every entry point below
  * ----------------------------------------------
  * Memory.  Every array argument is DEVICE memory owned by the caller, in the
- * layout stated (C order, densely packed), aligned to 16 bytes.  The library
- * allocates nothing and frees nothing.  Its only state is a call counter that
+ * layout stated (C order, densely packed), aligned to 16 bytes, unless its
+ * call says otherwise: the group arrays of pa_decode_shared_prefix and every
+ * block-manager argument are host memory, and pa_swap_blocks moves blocks to
+ * and from pinned host memory.  The library allocates nothing and frees
+ * nothing.  Its only state is a call counter that
  * tags the stream kernel's tickets and a cached compute-unit count per
  * device; every call is otherwise independent.
  *

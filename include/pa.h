@@ -298,8 +298,9 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
  * kernel scales row maxima of raw scores); a group's prefix may not exceed
  * max_blocks_per_seq blocks or max_seq_len tokens.  Errors: bad host
  * arguments -> PA_ERR_INVALID_ARG; more than PA_MAX_PREFIX_GROUPS groups or
- * an unsupported shape -> PA_ERR_UNSUPPORTED.  Three launches on `stream`
- * (prefix attention, tail decode, merge); allocates nothing.
+ * an unsupported shape -> PA_ERR_UNSUPPORTED.  Two launches on `stream`
+ * (the prefix attention and the tail decode in one, then the merge);
+ * allocates nothing.
  */
 #define PA_MAX_PREFIX_GROUPS 32
 pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,

@@ -50,14 +50,47 @@ def cxx() -> str:
     raise RuntimeError("no host C++ compiler (set CXX)")
 
 
+# The compiler's per-kernel resource report (registers, scratch, occupancy).
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def kernel_resources(remarks: str) -> dict:
+    """Per-kernel fields of the resource report in a compiler's stderr:
+    {kernel symbol: {"VGPRs": int, "ScratchSize [bytes/lane]": int, ...}}."""
+    out: dict = {}
+    cur = None
+    for line in remarks.splitlines():
+        if "remark:" not in line or "kernel-resource-usage" not in line:
+            continue
+        body = line.split("remark:", 1)[1].rsplit("[-Rpass-analysis", 1)[0].strip()
+        key, _, val = body.partition(":")
+        key, val = key.strip(), val.strip()
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            try:
+                cur[key] = int(val)
+            except ValueError:
+                cur[key] = val
+    return out
+
+
 def _compile(src: str, obj: str) -> None:
     if src.endswith(".cpp"):
         cmd = [cxx(), *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     else:
-        cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        cmd = [hipcc(), *HIP_FLAGS, RESOURCE_REMARKS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if src.endswith(".hip"):
+        # Every kernel is register-budgeted: a spill to scratch is a build
+        # error.  Besides its cost, it would put vector memory operations in
+        # the prefill key loop, whose direct LDS staging counts them.
+        spilled = {k: v for k, v in kernel_resources(res.stderr).items()
+                   if v.get("ScratchSize [bytes/lane]", 0) != 0}
+        if spilled:
+            raise RuntimeError(f"{os.path.basename(src)}: kernels spill to scratch: {spilled}")
 
 
 def build(verbose: bool = False) -> str:

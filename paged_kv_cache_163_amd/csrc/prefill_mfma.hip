@@ -14,10 +14,9 @@
 // kPrefillRows rows; each wave owns kRowTiles 16-row column tiles of the MFMA
 // step from mfma_step.h (S^T = K Q^T, O^T += V^T P^T) with its Q^T operands in
 // registers.  The work-group walks the keys [0, last position of its rows]
-// in 32-token steps: every thread loads 16-byte parts of the next step's K
-// and V tiles from HBM while the waves compute the current one from LDS
-// (double-buffered, one barrier per step), so each K/V byte is fetched once
-// per work-group.  A wave whose rows end earlier skips the math of the later
+// in 32-token steps, staged straight from HBM into four LDS buffers three
+// steps ahead of the math (row_tiles.h), so each K/V byte is fetched once per
+// work-group.  A wave whose rows end earlier skips the math of the later
 // steps.  The causal limit is per lane (a lane's score column is one row); V
 // rows past the wave's last key are zeroed so tail slots never reach the
 // sum.  The first step holds key 0, which every row sees, so no row's
@@ -87,24 +86,6 @@ void prefill_mfma_kernel(PrefillParams p) {
   // below kend).
   const int kfull = pos0 + wi_first;
 
-  // Q^T operands of the lane's row in each tile (zero past the chunk) and the
-  // causal limit of that row.
-  u32x4 qb[kRowTiles][D / 32];
-  int lim[kRowTiles];
-#pragma unroll
-  for (int nr = 0; nr < kRowTiles; ++nr) {
-    const int row = wrow0 + 16 * nr + r16;
-    const int qi = i0 + row / G;
-    const int g = row - (row / G) * G;
-    const bool valid = qi < nq;
-    lim[nr] = valid ? pos0 + qi : 0;
-    const char* qrow =
-        (const char*)p.q + ((int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D) * 2 + q4 * 16;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-      qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
-  }
-
   SeqView c;
   const int64_t head_stride = (int64_t)p.block_size * D * 2;
   c.kbase = (const char*)p.k_cache + (int64_t)head * head_stride;
@@ -125,53 +106,94 @@ void prefill_mfma_kernel(PrefillParams p) {
     a[nr].m = -INFINITY;
   }
   bool bad = false;
-  // The key loop of attend_keys (row_tiles.h), written out in the kernel.
-  __shared__ __attribute__((aligned(16))) unsigned char sm_kv[2][2 * 32 * kKvStride<D>];
+  // The key loop.  Step i's tiles sit in buffer i % 4; the wave's staging of
+  // step i + 3 goes out right after the barrier of step i, into the buffer
+  // every wave finished reading before that barrier.
+  __shared__ __attribute__((aligned(1024))) unsigned char sm_b[kLdsBufs][kStepBytes<D>];
   {
-    const StagePlan<D> sp = stage_plan<D>(c, tid);
-    Stage<D> st;
-    stage_load<D>(st, sp, c, 0, bad);
-    stage_store<D>(st, sp, sm_kv[0]);
-    __syncthreads();
-    int buf = 0;
-    for (int base = 0; base < kend_wg; base += 32) {
-      const bool more = base + 32 < kend_wg;
-      if (more) stage_load<D>(st, sp, c, base + 32, bad);  // in flight during the math
-      if (base < kend) {
-        f32x4 s[kRowTiles][2];
-        step_scores<D>(s, sm_kv[buf], qb, r16, q4);
-        u32x4 av[D / 16];
-        read_v<D>(av, sm_kv[buf] + 32 * kKvStride<D>, r16, q4);
-        step_softmax_pv<D>(s, av, a, base, kend, kfull, lim, p.scale_log2, q4);
-      }
-      if (more) stage_store<D>(st, sp, sm_kv[buf ^ 1]);
-      __syncthreads();
-      buf ^= 1;
+    const DmaLane<D> dl = dma_lane<D>(wave, lane);
+    const uint32_t kl = dma_k_lane(r16, q4);
+    const uint32_t vl = kTileBytes<D> + dma_v_lane(r16, q4);
+    const int nsteps = (kend_wg + 31) >> 5;
+    // The first two steps' tiles are requested before the Q loads, so the
+    // two latencies overlap; the wait for Q then also covers them, and no
+    // other vector load is waited for in the loop.
+    dma_issue<D>(dl, c, wave, 0, bad, sm_b[0]);
+    if (nsteps > 1) dma_issue<D>(dl, c, wave, 32, bad, sm_b[1]);
+    // Q^T operands of the lane's row in each tile (zero past the chunk) and the
+    // causal limit of that row.
+    u32x4 qb[kRowTiles][D / 32];
+    int lim[kRowTiles];
+#pragma unroll
+    for (int nr = 0; nr < kRowTiles; ++nr) {
+      const int row = wrow0 + 16 * nr + r16;
+      const int qi = i0 + row / G;
+      const int g = row - (row / G) * G;
+      const bool valid = qi < nq;
+      lim[nr] = valid ? pos0 + qi : 0;
+      const char* qrow =
+          (const char*)p.q + ((int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D) * 2 + q4 * 16;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+        qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (nsteps > 2) dma_issue<D>(dl, c, wave, 64, bad, sm_b[2]);
+    // One step: wait for this wave's part of its tiles, make every wave's part
+    // visible (barrier), stage step + 3, compute.
+    auto run = [&](int step, auto tag) {
+      constexpr bool kMask = decltype(tag)::value;
+      dma_wait<D>(min(nsteps - 1 - step, 2));
+      lds_barrier();
+      if (step + 3 < nsteps) dma_issue<D>(dl, c, wave, 32 * (step + 3), bad, sm_b[(step + 3) & 3]);
+      const int base = 32 * step;
+      if (!kMask || base < kend) {
+        const unsigned char* cur = sm_b[step & 3];
+        f32x4 s[kRowTiles][2];
+        dma_scores<D>(s, cur + kl, qb);
+        u32x4 av[D / 16];
+        dma_read_v<D>(av, cur + vl);
+        step_softmax_pv<D, kMask>(s, av, a, base, kend, lim, p.scale_log2, q4);
+      }
+    };
+    // The steps every row of the wave sees whole (base + 31 <= kfull) come
+    // first and need no mask; the rest of the walk takes the masked step.
+    // Each wave meets one barrier per step in either loop.
+    const int nfull = wave_rows && kfull >= 31 ? min(nsteps, (kfull - 31) / 32 + 1) : 0;
+    int step = 0;
+    for (; step < nfull; ++step) run(step, MaskTag<false>{});
+    for (; step < nsteps; ++step) run(step, MaskTag<true>{});
   }
+  __syncthreads();   // every wave is done reading the buffers the output staging reuses
   if (!wave_rows) return;
 
-  // The output rows go through LDS (the staging buffers, free since the key
-  // loop's last barrier): each wave writes its 32 normalised bf16 rows there
-  // and stores them back in whole 16-byte parts, so every store instruction
-  // writes full rows (contiguous for the G heads of one query) instead of a
-  // 32-byte piece of 16 rows.  A wave reads only its own rows, and one wave's
-  // LDS operations complete in order.
-  constexpr int kOutStride = D * 2 + 16;       // bytes per staged row (padded)
+  // The output rows go through LDS (wave w uses staging buffer w, free after
+  // the barrier above; no staging is in flight): each wave writes its 32
+  // normalised bf16 rows there and stores them back in whole 16-byte parts,
+  // so every store instruction writes full rows (contiguous for the G heads
+  // of one query) instead of a 32-byte piece of 16 rows.  A wave reads only
+  // its own rows, and one wave's LDS operations complete in order.  Part k
+  // of staged row r sits at slot k ^ swz(r), which makes the 16-byte reads
+  // conflict-free (measured; a padded row stride leaves them 2-way).
+  constexpr int kOutStride = D * 2;            // bytes per staged row
   constexpr int kParts = D * 2 / 16;           // 16-byte parts per row
   constexpr int kRowsPerStore = 64 / kParts;   // rows one store instruction covers
-  static_assert(kPfWaves * kWaveRows * kOutStride <= 2 * 2 * 32 * kKvStride<D>, "fits");
-  unsigned char* ow = &sm_kv[0][0] + wave * kWaveRows * kOutStride;
+  static_assert(kWaveRows * kOutStride <= kStepBytes<D>, "fits");
+  static_assert(kParts == 16 || kParts == 8, "row swizzle");
+  auto swz = [](int r) { return kParts == 16 ? r & 15 : (r >> 1) & 7; };
+  unsigned char* ow = sm_b[wave];
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr) {
     const float inv = bad ? __builtin_nanf("") : 1.0f / a[nr].l[0];
-    // o[jt][rr] is head dim 16 jt + 4 q4 + rr of the lane's row
-    unsigned char* lrow = ow + (16 * nr + r16) * kOutStride + 8 * q4;
+    // o[jt][rr] is head dim 16 jt + 4 q4 + rr of the lane's row: part
+    // 2 jt + q4 / 2, byte 8 (q4 % 2) of it
+    const int lr = 16 * nr + r16;
+    unsigned char* lrow = ow + lr * kOutStride + 8 * (q4 & 1);
 #pragma unroll
     for (int jt = 0; jt < kVd; ++jt) {
       const f32x4 o = a[nr].o[jt];
-      *(u32x2*)(lrow + 32 * jt) = u32x2{pack_bf16(o[0] * inv, o[1] * inv),
-                                        pack_bf16(o[2] * inv, o[3] * inv)};
+      *(u32x2*)(lrow + 16 * ((2 * jt + (q4 >> 1)) ^ swz(lr))) =
+          u32x2{pack_bf16(o[0] * inv, o[1] * inv), pack_bf16(o[2] * inv, o[3] * inv)};
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -182,7 +204,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     const int row = wrow0 + lr;
     const int qi = i0 + row / G;
     const int g = row - (row / G) * G;
-    const u32x4 v = *(const u32x4*)(ow + lr * kOutStride + 16 * part);
+    const u32x4 v = *(const u32x4*)(ow + lr * kOutStride + 16 * (part ^ swz(lr)));
     if (qi < nq)
       *(u32x4*)(out + (int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D + 8 * part) = v;
   }

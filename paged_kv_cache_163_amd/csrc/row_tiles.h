@@ -5,12 +5,18 @@
 // A work-group of kPfWaves waves covers kPrefillRows query rows of one KV
 // head; each wave owns kRowTiles 16-row column tiles of the MFMA step from
 // mfma_step.h (S^T = K Q^T, O^T += V^T P^T) with its Q^T operands in
-// registers.  The work-group walks the keys in 32-token steps: every thread
-// loads 16-byte parts of the next step's K and V tiles from HBM while the
-// waves compute the current one from LDS (double-buffered, one barrier per
-// step), so each K/V byte is fetched once per work-group.  Row limits are
-// per lane (a lane's score column is one row); V rows past a wave's last key
-// are zeroed so tail slots never reach the sum.
+// registers.  The work-group walks the keys in 32-token steps and stages each
+// step's K and V tiles in LDS once for all its waves, so each K/V byte is
+// fetched once per work-group.  Two staging schemes share the math:
+//  * register staging (attend_keys): every thread loads 16-byte parts of the
+//    next step into registers during the math and stores them to the other
+//    of two LDS buffers (one barrier per step);
+//  * direct staging (Dma*): gfx950's global-to-LDS loads fill four LDS
+//    buffers three steps ahead with no register on the way (prefill).
+// Row limits are per lane (a lane's score column is one row); V rows past a
+// wave's last key are zeroed so tail slots never reach the sum.  The steps a
+// wave's rows all see whole come first and take an unmasked step; the
+// remaining steps take the masked one.
 #pragma once
 
 #include "mfma_step.h"
@@ -53,14 +59,29 @@ struct PfAcc {
 // bf16, and most steps skip the rescale of the accumulators.
 constexpr float kSlack = 8.0f;
 
+// Compile-time choice of the masked or unmasked step.
+template <bool B>
+struct MaskTag {
+  static constexpr bool value = B;
+};
+
 // Max over the four lanes that share r16 (one per 16-lane row of the wave).
+// The maxes are plain v_max_f32, written as assembly: fmaxf on values that
+// come from a lane swap adds two signaling-NaN quieting maxes per call, which
+// these operands (scores, or -inf) never need.
+__device__ inline float fmax_nonan(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ inline float row_max4(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmax_nonan(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t w = __float_as_uint(x);
   const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax_nonan(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -117,17 +138,27 @@ __device__ inline void read_v(u32x4 (&av)[D / 16], const unsigned char* vs, int 
 }
 
 // Softmax and PV of one 32-key step for all row tiles of a wave, from its
-// raw scores s.  Keys > lim[nr] (the lane's row position) are masked unless
-// the whole step lies at or before kfull, the wave's first row position; V
-// values of keys at or past kend are zeroed.
+// raw scores s.  kMask (a step that some row of the wave does not see whole:
+// it reaches past kfull, the wave's first row position) masks keys > lim[nr]
+// (the lane's row position) and zeroes the V values of keys at or past kend,
+// the wave's last key + 1; other steps need neither.  The row tiles go
+// through the step together with one wave-uniform rescale branch, so their
+// dependent max and exp chains interleave.
 // c = scale * log2(e) > 0 (the host rejects other scales), so the row max of
-// c*s is c times the max of s.
-template <int D>
+// c*s is c times the max of s.  A row tile whose keys are all masked in a
+// step has mx = -inf: its reference max stays and its probabilities are 0
+// (every tile sees a finite key in its first step).
+template <int D, bool kMask>
 __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&av)[D / 16],
-                                       PfAcc<D> (&a)[kRowTiles], int base, int kend, int kfull,
+                                       PfAcc<D> (&a)[kRowTiles], int base, int kend,
                                        const int (&lim)[kRowTiles], float c, int q4) {
   constexpr int kVd = D / 16;
-  if (base + 32 > kend) {  // zero the V values of keys past the wave's last key
+  float sv[kRowTiles][8];
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[nr][e] = s[nr][e >> 2][e & 3];
+  if constexpr (kMask) {
     uint32_t keep[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -138,38 +169,71 @@ __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&a
     for (int jt = 0; jt < kVd; ++jt)
 #pragma unroll
       for (int u = 0; u < 4; ++u) av[jt][u] &= keep[u];
-  }
-  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
-  for (int nr = 0; nr < kRowTiles; ++nr) {
-    float sv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sv[e] = s[nr][e >> 2][e & 3];
-    if (base + 31 > kfull) {  // wave-uniform: some row does not see the whole step
+    for (int nr = 0; nr < kRowTiles; ++nr)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = base + 16 * (e >> 2) + 4 * q4 + (e & 3);
-        sv[e] = tok <= lim[nr] ? sv[e] : -INFINITY;
+        sv[nr][e] = tok <= lim[nr] ? sv[nr][e] : -INFINITY;
       }
-    }
-    float mr = -INFINITY;
+  }
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  if constexpr (kMask) {  // rare: one row tile after the other
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mr = fmaxf(mr, sv[e]);
-    const float mx = row_max4(mr) * c;
-    if (__builtin_amdgcn_ballot_w64(mx > a[nr].m + kSlack) != 0) {  // wave-uniform
-      const float m_new = fmaxf(a[nr].m, mx);
+    for (int nr = 0; nr < kRowTiles; ++nr) {
+      float mr = sv[nr][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mr = fmaxf(mr, sv[nr][e]);
+      const float mx = row_max4(mr) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > a[nr].m + kSlack) != 0) {  // wave-uniform
+        const float m_new = fmaxf(a[nr].m, mx);
+        const float keep = __builtin_amdgcn_exp2f(a[nr].m - m_new);
+#pragma unroll
+        for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] *= keep;
+        a[nr].l *= keep;
+        a[nr].m = m_new;
+      }
+      const float nm = -a[nr].m;
+      u32x4 pb;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        pb[u] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u], c, nm)),
+                          __builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u + 1], c, nm)));
+      a[nr].l = mma(ones, pb, a[nr].l);
+#pragma unroll
+      for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt]);
+    }
+    return;
+  }
+  float mx[kRowTiles];
+  bool grow = false;
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
+    float mr = sv[nr][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mr = fmaxf(mr, sv[nr][e]);
+    mx[nr] = row_max4(mr) * c;
+    grow |= mx[nr] > a[nr].m + kSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
+#pragma unroll
+    for (int nr = 0; nr < kRowTiles; ++nr) {
+      const float m_new = fmaxf(a[nr].m, mx[nr]);
       const float keep = __builtin_amdgcn_exp2f(a[nr].m - m_new);  // 0 on the first step
 #pragma unroll
       for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] *= keep;
       a[nr].l *= keep;
       a[nr].m = m_new;
     }
+  }
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr) {
     const float nm = -a[nr].m;
     u32x4 pb;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      pb[u] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sv[2 * u], c, nm)),
-                        __builtin_amdgcn_exp2f(fmaf(sv[2 * u + 1], c, nm)));
+      pb[u] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u], c, nm)),
+                        __builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u + 1], c, nm)));
     a[nr].l = mma(ones, pb, a[nr].l);
 #pragma unroll
     for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt]);
@@ -257,20 +321,205 @@ __device__ inline void attend_keys(PfAcc<D> (&a)[kRowTiles], const SeqView& c,
   stage_store<D>(st, sp, sm_kv[0]);
   __syncthreads();
   int buf = 0;
-  for (int base = kstart; base < kend_wg; base += 32) {
+  auto run = [&](int base, auto tag) {
+    constexpr bool kMask = decltype(tag)::value;
     const bool more = base + 32 < kend_wg;
     if (more) stage_load<D>(st, sp, c, base + 32, bad);  // in flight during the math
-    if (base < kend) {
+    if (!kMask || base < kend) {
       f32x4 s[kRowTiles][2];
       step_scores<D>(s, sm_kv[buf], qb, r16, q4);
       u32x4 av[D / 16];
       read_v<D>(av, sm_kv[buf] + 32 * kKvStride<D>, r16, q4);
-      step_softmax_pv<D>(s, av, a, base, kend, kfull, lim, scale_log2, q4);
+      step_softmax_pv<D, kMask>(s, av, a, base, kend, lim, scale_log2, q4);
     }
     if (more) stage_store<D>(st, sp, sm_kv[buf ^ 1]);
     __syncthreads();
     buf ^= 1;
+  };
+  // Steps every row sees whole (base + 31 <= kfull) first, without the mask;
+  // every wave meets one barrier per step in either loop.
+  int base = kstart;
+  for (; base < kend_wg && base + 31 <= kfull && base < kend; base += 32) run(base, MaskTag<false>{});
+  for (; base < kend_wg; base += 32) run(base, MaskTag<true>{});
+}
+
+
+// Direct global-to-LDS staging (global_load_lds_dwordx4).  One instruction
+// moves 16 bytes per lane straight into LDS: lane l's bytes land at the
+// wave-uniform LDS address + 16 l, so each instruction fills one contiguous
+// 1 KiB block.  A step's K and V tiles are D/16 such blocks each (K first);
+// block j of a tile holds the 16-byte chunks 2j and 2j + 1 of all 32 rows,
+// chunk c of row r at lane
+//   16 (2 (r / 16) + (c & 1)) + (r % 16)               in a K block,
+//   16 (2 (r / 16) + (c & 1)) + ((r % 16) ^ 8 (c & 1)) in a V block.
+// Measured with a bank-conflict probe on gfx950: the K operand reads
+// (ds_read_b128, 16 rows of one chunk) are conflict-free on the plain layout
+// and 2-way on the XOR one, the V transpose reads (ds_read_b64_tr_b16, rows
+// 0..7 of chunks 2j and 2j + 1 per half-wave) the other way round.  Wave w
+// issues blocks w, w + kPfWaves, ... of a step.
+constexpr int kLdsBufs = 4;                        // LDS buffers; steps staged ahead: 3
+template <int D>
+constexpr int kTileBytes = 32 * D * 2;             // one K or V tile of a step
+template <int D>
+constexpr int kStepBytes = 2 * kTileBytes<D>;
+template <int D>
+constexpr int kDmaPerWave = kStepBytes<D> / 1024 / kPfWaves;
+static_assert(kStepBytes<64> % (1024 * kPfWaves) == 0, "whole blocks per wave");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A lane's fixed part of its staging addresses.
+template <int D>
+struct DmaLane {
+  uint32_t off[kDmaPerWave<D>];  // byte offset inside the 16-token block tile
+  bool hi;                       // the lane's row is in the step's second 16-token tile
+  bool v[kDmaPerWave<D>];        // wave-uniform: the instruction stages V
+};
+
+template <int D>
+__device__ inline DmaLane<D> dma_lane(int wave, int lane) {
+  DmaLane<D> dl;
+  const int g = lane >> 4;
+  const int b = g & 1;
+  dl.hi = g >= 2;
+#pragma unroll
+  for (int u = 0; u < kDmaPerWave<D>; ++u) {
+    const int bi = u * kPfWaves + wave;
+    const int j = bi % (D / 16);
+    dl.v[u] = bi >= D / 16;
+    const int rr = dl.v[u] ? (lane & 15) ^ (8 * b) : lane & 15;  // row in the 16-token tile
+    dl.off[u] = (uint32_t)(rr * (D * 2) + 16 * (2 * j + b));
   }
+  return dl;
+}
+
+// Two block-table entries through the scalar cache.  The compiler would read
+// them with vector loads (the staging instructions count as possible writes to
+// global memory), whose waits would also wait for the staging in flight.
+__device__ inline void table_pair(int (&phys)[2], const int32_t* a, const int32_t* b) {
+  int x, y;
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(x), "=&s"(y)
+               : "s"(a), "s"(b)
+               : "memory");
+  phys[0] = x;
+  phys[1] = y;
+}
+
+// Work-group barrier that orders LDS only: the staging instructions in flight
+// (counted by vmcnt) are waited for explicitly by dma_wait, not here.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One 16-byte-per-lane direct load into LDS (lane l's bytes at lds + 16 l;
+// M0 holds the wave-uniform LDS address and is restored afterwards).
+// Written as inline assembly so that the compiler does not track it: its own
+// tracking waits for every staging load in flight before the LDS transpose
+// reads of any buffer.  Completion is awaited explicitly (dma_wait) before a
+// buffer is read.
+__device__ inline void dma16(const char* src, unsigned char* lds) {
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)lds;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(m)
+      : "memory");
+}
+
+// Issue the wave's kDmaPerWave blocks of the step at key `base` into the LDS
+// buffer `buf`.  Keys past the sequence re-read its last live block (masked
+// later); a table entry outside the pool sets `bad` (work-group uniform) and
+// reads block 0 instead.
+template <int D>
+__device__ inline void dma_issue(const DmaLane<D>& dl, const SeqView& c, int wave, int base,
+                                 bool& bad, unsigned char* buf) {
+  int phys[2];
+  table_pair(phys, c.table + min(base >> c.block_shift, c.nblocks_valid - 1),
+             c.table + min((base + 16) >> c.block_shift, c.nblocks_valid - 1));
+  int64_t tile[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int tok0 = base + 16 * kt;
+    if (phys[kt] < 0 || phys[kt] >= c.num_blocks) {
+      bad = true;
+      phys[kt] = 0;
+    }
+    tile[kt] = (int64_t)phys[kt] * c.block_stride + (int64_t)(tok0 & c.bmask) * (D * 2);
+  }
+  const int64_t t = dl.hi ? tile[1] : tile[0];
+  const char* kp = c.kbase + t;
+  const char* vp = c.vbase + t;
+#pragma unroll
+  for (int u = 0; u < kDmaPerWave<D>; ++u) {
+    const int bi = u * kPfWaves + wave;
+    dma16((dl.v[u] ? vp : kp) + dl.off[u], buf + 1024 * bi);
+  }
+}
+
+// Byte offsets of lane (r16, q4)'s K operand reads (row 16 kt + r16, chunk
+// 4 i + q4, at + 2048 i + 512 kt) and V transpose reads (key 4 q4 + r16 / 4
+// (+ 16), head dims 16 jt + 4 (r16 % 4) .. + 3, at + 1024 jt (+ 512)) in a
+// staged step; the V offset is relative to the V tile.
+__device__ inline uint32_t dma_k_lane(int r16, int q4) {
+  return 1024 * (q4 >> 1) + 256 * (q4 & 1) + 16 * r16;
+}
+__device__ inline uint32_t dma_v_lane(int r16, int q4) {
+  const int b = (r16 >> 1) & 1;
+  const int R = 4 * q4 + (r16 >> 2);
+  return 16 * (16 * b + (R ^ (8 * b))) + 8 * (r16 & 1);
+}
+
+// step_scores and read_v over the directly staged layout.
+template <int D>
+__device__ inline void dma_scores(f32x4 (&s)[kRowTiles][2], const unsigned char* ks,
+                                  const u32x4 (&qb)[kRowTiles][D / 32]) {
+#pragma unroll
+  for (int nr = 0; nr < kRowTiles; ++nr)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[nr][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const u32x4 k = *(const u32x4*)(ks + 2048 * i + 512 * kt);
+#pragma unroll
+      for (int nr = 0; nr < kRowTiles; ++nr) s[nr][kt] = mma(k, qb[nr][i], s[nr][kt]);
+    }
+}
+
+template <int D>
+__device__ inline void dma_read_v(u32x4 (&av)[D / 16], const unsigned char* v0) {
+#pragma unroll
+  for (int jt = 0; jt < D / 16; ++jt) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 1024 * jt));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 1024 * jt + 512));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+    av[jt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+}
+
+// Wait for this wave's staging of the current step, leaving the `later`
+// (0, 1 or 2) following steps' kDmaPerWave instructions each in flight.  The
+// count is exact because vector loads complete in order and the key loop
+// issues no other vector memory instruction after the first staging
+// (another load would only make the wait stricter).
+template <int D>
+__device__ inline void dma_wait(int later) {
+  if (later >= 2)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * kDmaPerWave<D>) & 15) | (((2 * kDmaPerWave<D>) >> 4) << 14));
+  else if (later == 1)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaPerWave<D> & 15));
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 }  // namespace

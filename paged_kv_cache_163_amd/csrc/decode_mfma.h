@@ -142,17 +142,29 @@ __device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_his
 // workspace unless the sequence has no prefix and one partition.
 enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered, kModeTail };
 
+// The LDS of one decode work-group, declared by the kernel that runs it (the
+// shared-prefix launch overlays it with the prefix work-groups' staging).
+template <int D>
+struct DecodeLds {
+  float o[kWaves][16][D];  // per-wave (m, l, O) for the cross-wave merge
+  float m[kWaves][16];
+  float l[kWaves][16];
+  int hist[256];           // longest-first ranking
+  int pick[2];
+  __attribute__((aligned(16))) unsigned char nw[2 * D * 2];  // fused append: the new K and V rows
+};
+
 // The work of decode work-group `wg` (sequence, KV head, partition) in mode M.
 template <int D, int M>
-__device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg) {
+__device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeLds<D>& lds) {
   constexpr int kKi = D / 32;
   constexpr bool kFused = M == kModeFused;
-  __shared__ float sm_o[kWaves][16][D];
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ int sm_hist[256];
-  __shared__ int sm_pick[2];
-  __shared__ __attribute__((aligned(16))) unsigned char sm_new[2 * D * 2];  // fused append
+  auto& sm_o = lds.o;
+  auto& sm_m = lds.m;
+  auto& sm_l = lds.l;
+  int* sm_hist = lds.hist;
+  int* sm_pick = lds.pick;
+  unsigned char* sm_new = lds.nw;
   WorkItem w = decode_work_item(p, wg);
   Ranked rk;
   if constexpr (M == kModeOrdered) {

@@ -11,7 +11,8 @@ __global__ __launch_bounds__(kWaves * 64)
 __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES_PER_EU)))
 #endif
 void decode_mfma_kernel(DecodeParams p) {
-  decode_wg<D, M>(p, blockIdx.x);
+  __shared__ DecodeLds<D> lds;
+  decode_wg<D, M>(p, blockIdx.x, lds);
 }
 
 }  // namespace

@@ -106,24 +106,11 @@ void prefill_mfma_kernel(PrefillParams p) {
     a[nr].m = -INFINITY;
   }
   bool bad = false;
-  // The key loop.  Step i's tiles sit in buffer i % 4; the wave's staging of
-  // step i + 3 goes out right after the barrier of step i, into the buffer
-  // every wave finished reading before that barrier.
-  __shared__ __attribute__((aligned(1024))) unsigned char sm_b[kLdsBufs][kStepBytes<D>];
-  {
-    const DmaLane<D> dl = dma_lane<D>(wave, lane);
-    const uint32_t kl = dma_k_lane(r16, q4);
-    const uint32_t vl = kTileBytes<D> + dma_v_lane(r16, q4);
-    const int nsteps = (kend_wg + 31) >> 5;
-    // The first two steps' tiles are requested before the Q loads, so the
-    // two latencies overlap; the wait for Q then also covers them, and no
-    // other vector load is waited for in the loop.
-    dma_issue<D>(dl, c, wave, 0, bad, sm_b[0]);
-    if (nsteps > 1) dma_issue<D>(dl, c, wave, 32, bad, sm_b[1]);
-    // Q^T operands of the lane's row in each tile (zero past the chunk) and the
-    // causal limit of that row.
-    u32x4 qb[kRowTiles][D / 32];
-    int lim[kRowTiles];
+  // Q^T operands of the lane's row in each tile (zero past the chunk) and the
+  // causal limit of that row, loaded while the first key tiles are in flight.
+  u32x4 qb[kRowTiles][D / 32];
+  int lim[kRowTiles];
+  auto load_q = [&] {
 #pragma unroll
     for (int nr = 0; nr < kRowTiles; ++nr) {
       const int row = wrow0 + 16 * nr + r16;
@@ -131,39 +118,16 @@ void prefill_mfma_kernel(PrefillParams p) {
       const int g = row - (row / G) * G;
       const bool valid = qi < nq;
       lim[nr] = valid ? pos0 + qi : 0;
-      const char* qrow =
-          (const char*)p.q + ((int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D) * 2 + q4 * 16;
+      const char* qrow = (const char*)p.q +
+                         ((int64_t)(q0 + qi) * row_stride + head0 + (int64_t)g * D) * 2 + q4 * 16;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
         qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    if (nsteps > 2) dma_issue<D>(dl, c, wave, 64, bad, sm_b[2]);
-    // One step: wait for this wave's part of its tiles, make every wave's part
-    // visible (barrier), stage step + 3, compute.
-    auto run = [&](int step, auto tag) {
-      constexpr bool kMask = decltype(tag)::value;
-      dma_wait<D>(min(nsteps - 1 - step, 2));
-      lds_barrier();
-      if (step + 3 < nsteps) dma_issue<D>(dl, c, wave, 32 * (step + 3), bad, sm_b[(step + 3) & 3]);
-      const int base = 32 * step;
-      if (!kMask || base < kend) {
-        const unsigned char* cur = sm_b[step & 3];
-        f32x4 s[kRowTiles][2];
-        dma_scores<D>(s, cur + kl, qb);
-        u32x4 av[D / 16];
-        dma_read_v<D>(av, cur + vl);
-        step_softmax_pv<D, kMask>(s, av, a, base, kend, lim, p.scale_log2, q4);
-      }
-    };
-    // The steps every row of the wave sees whole (base + 31 <= kfull) come
-    // first and need no mask; the rest of the walk takes the masked step.
-    // Each wave meets one barrier per step in either loop.
-    const int nfull = wave_rows && kfull >= 31 ? min(nsteps, (kfull - 31) / 32 + 1) : 0;
-    int step = 0;
-    for (; step < nfull; ++step) run(step, MaskTag<false>{});
-    for (; step < nsteps; ++step) run(step, MaskTag<true>{});
-  }
+  };
+  __shared__ __attribute__((aligned(1024))) unsigned char sm_b[kLdsBufs][kStepBytes<D>];
+  attend_keys<D>(a, c, qb, lim, 0, kend_wg, kend, kfull, wave_rows, p.scale_log2, bad, sm_b, wave,
+                 lane, load_q);
   __syncthreads();   // every wave is done reading the buffers the output staging reuses
   if (!wave_rows) return;
 

@@ -5,18 +5,14 @@
 // A work-group of kPfWaves waves covers kPrefillRows query rows of one KV
 // head; each wave owns kRowTiles 16-row column tiles of the MFMA step from
 // mfma_step.h (S^T = K Q^T, O^T += V^T P^T) with its Q^T operands in
-// registers.  The work-group walks the keys in 32-token steps and stages each
-// step's K and V tiles in LDS once for all its waves, so each K/V byte is
-// fetched once per work-group.  Two staging schemes share the math:
-//  * register staging (attend_keys): every thread loads 16-byte parts of the
-//    next step into registers during the math and stores them to the other
-//    of two LDS buffers (one barrier per step);
-//  * direct staging (Dma*): gfx950's global-to-LDS loads fill four LDS
-//    buffers three steps ahead with no register on the way (prefill).
-// Row limits are per lane (a lane's score column is one row); V rows past a
-// wave's last key are zeroed so tail slots never reach the sum.  The steps a
-// wave's rows all see whole come first and take an unmasked step; the
-// remaining steps take the masked one.
+// registers.  The work-group walks the keys in 32-token steps (attend_keys)
+// and stages each step's K and V tiles in LDS once for all its waves, so each
+// K/V byte is fetched once per work-group: gfx950's global-to-LDS loads fill
+// four LDS buffers three steps ahead of the math, with no register on the
+// way.  Row limits are per lane (a lane's score column is one row); V rows
+// past a wave's last key are zeroed so tail slots never reach the sum.  The
+// steps a wave's rows all see whole come first and take an unmasked step;
+// the remaining steps take the masked one.
 #pragma once
 
 #include "mfma_step.h"
@@ -27,22 +23,9 @@ namespace {
 using namespace mfma;
 
 constexpr int kPfWaves = 4;
-constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kRowTiles = 2;                 // 16-row MFMA column tiles per wave
 constexpr int kWaveRows = 16 * kRowTiles;
 static_assert(kPfWaves * kWaveRows == kPrefillRows, "work-group rows");
-// LDS bytes per staged K or V row: padding moves consecutive rows to other
-// banks, so the lanes that read one 16-byte column of 16 rows collide less
-// (32 bytes measured best of 0, 16, 32, 48 and 64).
-template <int D>
-constexpr int kKvStride = D * 2 + 32;
-template <int D>
-constexpr int kRowParts = D * 2 / 16;        // 16-byte parts of a K or V row
-template <int D>
-constexpr int kStageParts = 2 * 32 * kRowParts<D> / kPfThreads;  // per thread per step
-static_assert(2 * 32 * kRowParts<128> % kPfThreads == 0 && 2 * 32 * kRowParts<64> % kPfThreads == 0,
-              "every thread stages whole parts");
-
 // A row's running state: O^T tiles, the row sum (computed on the matrix core
 // as P^T against a ones operand, so it is the exact sum of the bf16 P the
 // output uses; all four elements hold the lane's row sum) and the reference
@@ -91,51 +74,8 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {  // round to nearest 
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Scores S^T = K Q^T of one 32-key step for every row tile of a wave, raw
-// (unscaled): s[nr][kt][j] is key 16 kt + 4 q4 + j of the step for the
-// lane's row of tile nr.  K: lane (r16, q4) reads staged row 16 kt + r16,
-// head dims 32 i + 8 q4 .. + 7, once for all row tiles.
-template <int D>
-__device__ inline void step_scores(f32x4 (&s)[kRowTiles][2], const unsigned char* ks,
-                                   const u32x4 (&qb)[kRowTiles][D / 32], int r16, int q4) {
-#pragma unroll
-  for (int nr = 0; nr < kRowTiles; ++nr)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) s[nr][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const u32x4 k = *(const u32x4*)(ks + (16 * kt + r16) * kKvStride<D> + 64 * i + 16 * q4);
-#pragma unroll
-      for (int nr = 0; nr < kRowTiles; ++nr) s[nr][kt] = mma(k, qb[nr][i], s[nr][kt]);
-    }
-}
-
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// The V^T operands of one step (A operands of the PV MFMAs).  Tile jt covers
-// head dims 16 jt .. 16 jt + 15: lane (r16, q4) holds d = 16 jt + r16 for the
-// step's keys tau(q4, e) = 16 (e / 4) + 4 q4 + e % 4, e = 0..7, the order
-// the score tiles leave P^T in.  The LDS transpose read (ds_read_b64_tr_b16)
-// hands lane 4 b + c of each 16-lane group element c of the 8-byte rows that
-// lanes b, b + 4, b + 8 and b + 12 of the group address; lane (r16, q4)
-// addresses key 4 q4 + r16 / 4 (16 more for the second read) at head dims
-// 16 jt + 4 (r16 % 4) .. + 3.
-template <int D>
-__device__ inline void read_v(u32x4 (&av)[D / 16], const unsigned char* vs, int r16, int q4) {
-  const unsigned char* v0 = vs + (4 * q4 + (r16 >> 2)) * kKvStride<D> + 8 * (r16 & 3);
-#pragma unroll
-  for (int jt = 0; jt < D / 16; ++jt) {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * jt));
-    const i16x4 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 16 * kKvStride<D> + 32 * jt));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-    av[jt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
-  }
-}
 
 // Softmax and PV of one 32-key step for all row tiles of a wave, from its
 // raw scores s.  kMask (a step that some row of the wave does not see whole:
@@ -239,110 +179,6 @@ __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&a
     for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt]);
   }
 }
-
-// The K and V tiles of one 32-key step, staged by the whole work-group:
-// thread t holds parts t, t + kPfThreads, ... of the step's 2*32 rows (K rows
-// first), 16 bytes each.  A part keeps its row, column and K|V role from step
-// to step, so its byte offsets inside the block tile and inside the LDS tile
-// are fixed per thread (StagePlan); a step only adds the two 16-token tiles'
-// block offsets.  Keys past the sequence re-read its last live block (masked
-// later); a table entry outside the pool sets `bad` (work-group uniform) and
-// reads block 0 instead.
-template <int D>
-struct Stage {
-  u32x4 part[kStageParts<D>];
-};
-
-template <int D>
-struct StagePlan {
-  const char* src[kStageParts<D>];   // K or V base + row-in-tile and column offset
-  uint32_t lds[kStageParts<D>];      // byte offset in an LDS tile
-  bool hi[kStageParts<D>];           // the part's row is in the step's second 16-token tile
-};
-
-template <int D>
-__device__ inline StagePlan<D> stage_plan(const SeqView& c, int tid) {
-  StagePlan<D> sp;
-#pragma unroll
-  for (int j = 0; j < kStageParts<D>; ++j) {
-    const int idx = tid + kPfThreads * j;
-    const int kv = idx / (32 * kRowParts<D>);
-    const int rem = idx - kv * 32 * kRowParts<D>;
-    const int row = rem / kRowParts<D>;
-    const int col = rem - row * kRowParts<D>;
-    sp.src[j] = (kv ? c.vbase : c.kbase) + (row & 15) * (D * 2) + col * 16;
-    sp.lds[j] = (uint32_t)((kv * 32 + row) * kKvStride<D> + col * 16);
-    sp.hi[j] = row >= 16;
-  }
-  return sp;
-}
-
-template <int D>
-__device__ inline void stage_load(Stage<D>& st, const StagePlan<D>& sp, const SeqView& c,
-                                  int base, bool& bad) {
-  int64_t tile[2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int tok0 = base + 16 * kt;
-    const int lb = min(tok0 >> c.block_shift, c.nblocks_valid - 1);
-    int phys = c.table[lb];
-    if (phys < 0 || phys >= c.num_blocks) {
-      bad = true;
-      phys = 0;
-    }
-    tile[kt] = (int64_t)phys * c.block_stride + (int64_t)(tok0 & c.bmask) * (D * 2);
-  }
-#pragma unroll
-  for (int j = 0; j < kStageParts<D>; ++j)
-    st.part[j] = *(const u32x4*)(sp.src[j] + (sp.hi[j] ? tile[1] : tile[0]));
-}
-
-template <int D>
-__device__ inline void stage_store(const Stage<D>& st, const StagePlan<D>& sp, unsigned char* buf) {
-#pragma unroll
-  for (int j = 0; j < kStageParts<D>; ++j) *(u32x4*)(buf + sp.lds[j]) = st.part[j];
-}
-
-// The work-group's walk over keys [kstart, kend_wg) in 32-key steps (kstart
-// a multiple of 32): every thread stages its parts of the next step's K and V
-// tiles from HBM while the waves compute the current one from LDS (two
-// buffers, one barrier per step).  A wave takes the math of the steps below
-// its own kend only; every wave stages and meets every barrier.
-template <int D>
-__device__ inline void attend_keys(PfAcc<D> (&a)[kRowTiles], const SeqView& c,
-                                   const u32x4 (&qb)[kRowTiles][D / 32],
-                                   const int (&lim)[kRowTiles], int kstart, int kend_wg, int kend,
-                                   int kfull, float scale_log2, bool& bad,
-                                   unsigned char (*sm_kv)[2 * 32 * kKvStride<D>], int tid, int r16,
-                                   int q4) {
-  const StagePlan<D> sp = stage_plan<D>(c, tid);
-  Stage<D> st;
-  stage_load<D>(st, sp, c, kstart, bad);
-  stage_store<D>(st, sp, sm_kv[0]);
-  __syncthreads();
-  int buf = 0;
-  auto run = [&](int base, auto tag) {
-    constexpr bool kMask = decltype(tag)::value;
-    const bool more = base + 32 < kend_wg;
-    if (more) stage_load<D>(st, sp, c, base + 32, bad);  // in flight during the math
-    if (!kMask || base < kend) {
-      f32x4 s[kRowTiles][2];
-      step_scores<D>(s, sm_kv[buf], qb, r16, q4);
-      u32x4 av[D / 16];
-      read_v<D>(av, sm_kv[buf] + 32 * kKvStride<D>, r16, q4);
-      step_softmax_pv<D, kMask>(s, av, a, base, kend, lim, scale_log2, q4);
-    }
-    if (more) stage_store<D>(st, sp, sm_kv[buf ^ 1]);
-    __syncthreads();
-    buf ^= 1;
-  };
-  // Steps every row sees whole (base + 31 <= kfull) first, without the mask;
-  // every wave meets one barrier per step in either loop.
-  int base = kstart;
-  for (; base < kend_wg && base + 31 <= kfull && base < kend; base += 32) run(base, MaskTag<false>{});
-  for (; base < kend_wg; base += 32) run(base, MaskTag<true>{});
-}
-
 
 // Direct global-to-LDS staging (global_load_lds_dwordx4).  One instruction
 // moves 16 bytes per lane straight into LDS: lane l's bytes land at the
@@ -477,9 +313,13 @@ __device__ inline uint32_t dma_v_lane(int r16, int q4) {
   return 16 * (16 * b + (R ^ (8 * b))) + 8 * (r16 & 1);
 }
 
-// step_scores and read_v over the directly staged layout.
+// Scores S^T = K Q^T of one 32-key step for every row tile of a wave, raw
+// (unscaled): s[nr][kt][j] is key 16 kt + 4 q4 + j of the step for the
+// lane's row of tile nr.  K: lane (r16, q4) reads row 16 kt + r16, head dims
+// 32 i + 8 q4 .. + 7, once for all row tiles; `ks` is the step's buffer plus
+// dma_k_lane.
 template <int D>
-__device__ inline void dma_scores(f32x4 (&s)[kRowTiles][2], const unsigned char* ks,
+__device__ inline void step_scores(f32x4 (&s)[kRowTiles][2], const unsigned char* ks,
                                   const u32x4 (&qb)[kRowTiles][D / 32]) {
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr)
@@ -495,8 +335,16 @@ __device__ inline void dma_scores(f32x4 (&s)[kRowTiles][2], const unsigned char*
     }
 }
 
+// The V^T operands of one step (A operands of the PV MFMAs).  Tile jt covers
+// head dims 16 jt .. 16 jt + 15: lane (r16, q4) holds d = 16 jt + r16 for the
+// step's keys tau(q4, e) = 16 (e / 4) + 4 q4 + e % 4, e = 0..7, the order
+// the score tiles leave P^T in.  The LDS transpose read (ds_read_b64_tr_b16)
+// hands lane 4 b + c of each 16-lane group element c of the 8-byte rows that
+// lanes b, b + 4, b + 8 and b + 12 of the group address; lane (r16, q4)
+// addresses key 4 q4 + r16 / 4 (16 more for the second read) at head dims
+// 16 jt + 4 (r16 % 4) .. + 3 (`v0`: the step's V tile plus dma_v_lane).
 template <int D>
-__device__ inline void dma_read_v(u32x4 (&av)[D / 16], const unsigned char* v0) {
+__device__ inline void read_v(u32x4 (&av)[D / 16], const unsigned char* v0) {
 #pragma unroll
   for (int jt = 0; jt < D / 16; ++jt) {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 1024 * jt));
@@ -520,6 +368,61 @@ __device__ inline void dma_wait(int later) {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (kDmaPerWave<D> & 15));
   else
     __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+
+// The work-group's walk over keys [kstart, kend_wg) in 32-key steps (kstart a
+// multiple of 32).  Step t sits in buffer t % kLdsBufs.  Opening step t means:
+// wait for this wave's part of its tiles, make every wave's part visible
+// (barrier), and stage step t + 3 into the buffer every wave finished reading
+// before that barrier.  The first two steps are requested before load_q()
+// issues the Q loads, so the latencies overlap; the loads are all waited for
+// before the walk, whose only vector memory instructions are then the staging.
+// A wave takes the math of the steps below its own kend only; every wave
+// stages and meets every barrier.  kfull is the wave's first row position:
+// the steps at or before it need no mask.
+template <int D, class LoadQ>
+__device__ inline void attend_keys(PfAcc<D> (&a)[kRowTiles], const SeqView& c,
+                                   const u32x4 (&qb)[kRowTiles][D / 32],
+                                   const int (&lim)[kRowTiles], int kstart, int kend_wg,
+                                   int kend, int kfull, bool wave_rows, float scale_log2,
+                                   bool& bad, unsigned char (*buf)[kStepBytes<D>], int wave,
+                                   int lane, LoadQ&& load_q) {
+  const int r16 = lane & 15;
+  const int q4 = lane >> 4;
+  const DmaLane<D> dl = dma_lane<D>(wave, lane);
+  const uint32_t kl = dma_k_lane(r16, q4);
+  const uint32_t vl = kTileBytes<D> + dma_v_lane(r16, q4);
+  const int nsteps = (kend_wg - kstart + 31) >> 5;
+  dma_issue<D>(dl, c, wave, kstart, bad, buf[0]);
+  if (nsteps > 1) dma_issue<D>(dl, c, wave, kstart + 32, bad, buf[1]);
+  load_q();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (nsteps > 2) dma_issue<D>(dl, c, wave, kstart + 64, bad, buf[2]);
+  auto run = [&](int t, auto tag) {
+    constexpr bool kMask = decltype(tag)::value;
+    dma_wait<D>(min(nsteps - 1 - t, 2));
+    lds_barrier();
+    if (t + 3 < nsteps)
+      dma_issue<D>(dl, c, wave, kstart + 32 * (t + 3), bad, buf[(t + 3) % kLdsBufs]);
+    const int base = kstart + 32 * t;
+    if (!kMask || base < kend) {
+      const unsigned char* cur = buf[t % kLdsBufs];
+      f32x4 s[kRowTiles][2];
+      step_scores<D>(s, cur + kl, qb);
+      u32x4 av[D / 16];
+      read_v<D>(av, cur + vl);
+      step_softmax_pv<D, kMask>(s, av, a, base, kend, lim, scale_log2, q4);
+    }
+  };
+  // Unmasked steps: base + 31 <= kfull (then also base < kend).  They come in
+  // a loop of their own, which keeps the register assignments of the two step
+  // kinds apart (one loop with both behind a branch spilled).
+  const int nfull =
+      wave_rows && kfull - kstart >= 31 ? min(nsteps, (kfull - kstart - 31) / 32 + 1) : 0;
+  int t = 0;
+  for (; t < nfull; ++t) run(t, MaskTag<false>{});
+  for (; t < nsteps; ++t) run(t, MaskTag<true>{});
 }
 
 }  // namespace

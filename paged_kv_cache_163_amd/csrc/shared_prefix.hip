@@ -36,7 +36,8 @@ using namespace mfma;
 // KV head) pair run on one XCD (x % 8 is kept from the launch index), so the
 // pair's K/V tiles stay in that XCD's L2.
 template <int D>
-__device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x) {
+__device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x,
+                                          unsigned char (*buf)[kStepBytes<D>]) {
   constexpr int kVd = D / 16;
   const PrefixGroups& pg = p.prefix;
   int grp = 0;
@@ -71,23 +72,6 @@ __device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x) {
   const int kend = wave_rows ? kend_wg : kstart;
   const int kfull = kend_wg - 1;
 
-  u32x4 qb[kRowTiles][D / 32];
-  int lim[kRowTiles];
-#pragma unroll
-  for (int nr = 0; nr < kRowTiles; ++nr) {
-    const int row = wrow0 + 16 * nr + r16;
-    const int mi = m0 + row / G;
-    const int g = row - (row / G) * G;
-    const bool valid = mi < members;
-    lim[nr] = kend_wg - 1;
-    const char* qrow = (const char*)p.q +
-                       (((int64_t)(first + mi) * p.num_heads + (int64_t)head * G + g) * D) * 2 +
-                       q4 * 16;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-      qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
-  }
-
   SeqView c;
   const int64_t head_stride = (int64_t)p.block_size * D * 2;
   c.kbase = (const char*)p.k_cache + (int64_t)head * head_stride;
@@ -108,9 +92,28 @@ __device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x) {
     a[nr].m = -INFINITY;
   }
   bool bad = false;
-  __shared__ __attribute__((aligned(16))) unsigned char sm_kv[2][2 * 32 * kKvStride<D>];
-  attend_keys<D>(a, c, qb, lim, kstart, kend_wg, kend, kfull, p.scale_log2, bad, sm_kv, tid,
-                 r16, q4);
+  // Q^T operands of the lane's row (a member's query head; zero past the
+  // group), loaded while the first key tiles are in flight.
+  u32x4 qb[kRowTiles][D / 32];
+  int lim[kRowTiles];
+  auto load_q = [&] {
+#pragma unroll
+    for (int nr = 0; nr < kRowTiles; ++nr) {
+      const int row = wrow0 + 16 * nr + r16;
+      const int mi = m0 + row / G;
+      const int g = row - (row / G) * G;
+      const bool valid = mi < members;
+      lim[nr] = kend_wg - 1;
+      const char* qrow = (const char*)p.q +
+                         (((int64_t)(first + mi) * p.num_heads + (int64_t)head * G + g) * D) * 2 +
+                         q4 * 16;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+        qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  attend_keys<D>(a, c, qb, lim, kstart, kend_wg, kend, kfull, wave_rows, p.scale_log2, bad, buf,
+                 wave, lane, load_q);
   if (!wave_rows) return;
 
 #pragma unroll
@@ -133,6 +136,16 @@ __device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x) {
 }
 
 
+// A work-group is one kind or the other, so the two share one LDS
+// allocation: the prefix part's four staging buffers (64 KB at head_dim 128)
+// or the decode work-group's merge space.  Two work-groups then fit a
+// compute unit.
+template <int D>
+union SharedPrefixLds {
+  unsigned char kv[kLdsBufs][kStepBytes<D>];
+  DecodeLds<D> tail;
+};
+
 // Two resident work-groups per compute unit (both kinds fit 256 registers
 // per lane; without the bound the allocator spends AGPRs and halves that).
 // Work-group x: the prefix attention's work-group x while x < prefix_wgs (a
@@ -140,11 +153,12 @@ __device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x) {
 template <int D>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void shared_prefix_kernel(DecodeParams p, int prefix_wgs) {
+  __shared__ __attribute__((aligned(1024))) SharedPrefixLds<D> lds;
   const int x = blockIdx.x;
   if (x < prefix_wgs)
-    prefix_wg<D>(p, x);
+    prefix_wg<D>(p, x, lds.kv);
   else
-    decode_wg<D, kModeTail>(p, x - prefix_wgs);
+    decode_wg<D, kModeTail>(p, x - prefix_wgs, lds.tail);
 }
 
 // Merge of each row's prefix partials (slots [0, kp), one per prefix

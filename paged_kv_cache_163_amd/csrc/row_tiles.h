@@ -26,6 +26,7 @@ constexpr int kPfWaves = 4;
 constexpr int kRowTiles = 2;                 // 16-row MFMA column tiles per wave
 constexpr int kWaveRows = 16 * kRowTiles;
 static_assert(kPfWaves * kWaveRows == kPrefillRows, "work-group rows");
+
 // A row's running state: O^T tiles, the row sum (computed on the matrix core
 // as P^T against a ones operand, so it is the exact sum of the bf16 P the
 // output uses; all four elements hold the lane's row sum) and the reference
@@ -394,6 +395,10 @@ __device__ inline void attend_keys(PfAcc<D> (&a)[kRowTiles], const SeqView& c,
   const uint32_t kl = dma_k_lane(r16, q4);
   const uint32_t vl = kTileBytes<D> + dma_v_lane(r16, q4);
   const int nsteps = (kend_wg - kstart + 31) >> 5;
+  if (nsteps <= 0) {  // no keys: nothing staged, so nothing in flight at exit
+    load_q();
+    return;
+  }
   dma_issue<D>(dl, c, wave, kstart, bad, buf[0]);
   if (nsteps > 1) dma_issue<D>(dl, c, wave, kstart + 32, bad, buf[1]);
   load_q();

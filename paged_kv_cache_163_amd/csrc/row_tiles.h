@@ -119,33 +119,6 @@ __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&a
       }
   }
   const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  if constexpr (kMask) {  // rare: one row tile after the other
-#pragma unroll
-    for (int nr = 0; nr < kRowTiles; ++nr) {
-      float mr = sv[nr][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mr = fmaxf(mr, sv[nr][e]);
-      const float mx = row_max4(mr) * c;
-      if (__builtin_amdgcn_ballot_w64(mx > a[nr].m + kSlack) != 0) {  // wave-uniform
-        const float m_new = fmaxf(a[nr].m, mx);
-        const float keep = __builtin_amdgcn_exp2f(a[nr].m - m_new);
-#pragma unroll
-        for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] *= keep;
-        a[nr].l *= keep;
-        a[nr].m = m_new;
-      }
-      const float nm = -a[nr].m;
-      u32x4 pb;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        pb[u] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u], c, nm)),
-                          __builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u + 1], c, nm)));
-      a[nr].l = mma(ones, pb, a[nr].l);
-#pragma unroll
-      for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt]);
-    }
-    return;
-  }
   float mx[kRowTiles];
   bool grow = false;
 #pragma unroll

@@ -6,11 +6,16 @@ size, head dim, dtype and partition size.  It then runs every kernel that
 supports the shape through the C ABI, and the pinned float64 oracle computes
 the reference from the same bytes.
 
+PA_RANDOM_SCALE=k (environment) runs k times as many cases of each kind
+(new seeds after the default ones), for a wider sweep.
+
 Bars as in test_gpu_parity.py:
 * copy-on-write copies and appends are bit-exact;
 * fp32 outputs within 1e-5 absolute;
 * bf16 outputs within 1e-2 + 2e-2 |ref|.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -23,6 +28,7 @@ from paged_kv_cache_163_amd import workloads as W  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+SCALE = max(1, int(os.environ.get("PA_RANDOM_SCALE", "1")))
 
 
 @pytest.fixture(scope="module")
@@ -70,7 +76,7 @@ def draw_lengths(rng, n, longest):
     return lens
 
 
-@pytest.mark.parametrize("case", range(40))
+@pytest.mark.parametrize("case", range(40 * SCALE))
 def test_random_decode_step(pa, case):
     rng = np.random.default_rng([20261202, 1, case])
     dtype = "f32" if rng.random() < 0.25 else "bf16"
@@ -112,7 +118,7 @@ def test_random_decode_step(pa, case):
         assert_close(oracle.to_f64(host(out)), ref, dtype, f"{what} {kernel}")
 
 
-@pytest.mark.parametrize("case", range(15))
+@pytest.mark.parametrize("case", range(15 * SCALE))
 def test_random_prefill(pa, case):
     rng = np.random.default_rng([20261202, 2, case])
     head_dim = int(rng.choice([64, 128]))
@@ -138,7 +144,7 @@ def test_random_prefill(pa, case):
                  f"chunks={chunks.tolist()} lens={lens.tolist()}")
 
 
-@pytest.mark.parametrize("case", range(15))
+@pytest.mark.parametrize("case", range(15 * SCALE))
 def test_random_shared_prefix(pa, case):
     rng = np.random.default_rng([20261202, 3, case])
     head_dim = int(rng.choice([64, 128]))
@@ -176,7 +182,7 @@ def test_random_shared_prefix(pa, case):
                  f"groups={bounds} prefix={prefix} P={ppart}")
 
 
-@pytest.mark.parametrize("case", range(20))
+@pytest.mark.parametrize("case", range(20 * SCALE))
 def test_random_fused_append(pa, case):
     """pa_decode_append: one new token per sequence (slot -1 for about one
     sequence in five, whose length then stays put), appended and decoded in

@@ -18,9 +18,12 @@
 namespace {
 
 constexpr int32_t kAbiVersion = 1;
-// Work-groups a decode launch should offer before sequences are split: four
-// four-wave work-groups per compute unit on a 256-CU MI355X.
-constexpr int64_t kTargetWorkgroups = 1024;
+// Work-groups a decode launch should offer before sequences are split: the
+// two resident four-wave work-groups per compute unit of a 256-CU MI355X.
+// Measured on 16 sequences x 8,192 tokens x 8 KV heads: 89 us at 2,048-token
+// partitions (512 work-groups) against 91 us at 1,024 (1,024 work-groups,
+// more partials to merge) and 129 us unsplit (128 work-groups).
+constexpr int64_t kTargetWorkgroups = 512;
 constexpr int32_t kMfmaStep = 32;  // tokens per MFMA-kernel step
 constexpr int64_t kMaxPartitions = 16384;  // partitions per sequence (split kernels)
 constexpr int32_t kStreamWgsPerCu = 2;   // resident 4-wave work-groups per CU

@@ -140,18 +140,32 @@ __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&a
       a[nr].m = m_new;
     }
   }
+  // Tile 0's probabilities first.  Its products then go to the matrix cores a
+  // few at a time, each group followed by one packed pair of tile 1's
+  // exponentials: the products do not depend on them, so the wave keeps the
+  // matrix and vector pipes busy at once instead of one after the other.
+  static_assert(kRowTiles == 2 && kVd % 4 == 0, "two row tiles, whole groups");
+  u32x4 pb[kRowTiles];
+  auto probs = [&](int nr, int u) {
+    pb[nr][u] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u], c, -a[nr].m)),
+                          __builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u + 1], c, -a[nr].m)));
+  };
 #pragma unroll
-  for (int nr = 0; nr < kRowTiles; ++nr) {
-    const float nm = -a[nr].m;
-    u32x4 pb;
+  for (int u = 0; u < 4; ++u) probs(0, u);
+  a[0].l = mma(ones, pb[0], a[0].l);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      pb[u] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u], c, nm)),
-                        __builtin_amdgcn_exp2f(fmaf(sv[nr][2 * u + 1], c, nm)));
-    a[nr].l = mma(ones, pb, a[nr].l);
-#pragma unroll
-    for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = mma(av[jt], pb, a[nr].o[jt]);
+  for (int jt = 0; jt < kVd; ++jt) {
+    __builtin_amdgcn_sched_barrier(0);
+    a[0].o[jt] = mma(av[jt], pb[0], a[0].o[jt]);
+    if (jt % (kVd / 4) == kVd / 4 - 1) {
+      probs(1, jt / (kVd / 4));
+      asm volatile("" : "+v"(pb[1][jt / (kVd / 4)]));  // computed here, not at its use
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  a[1].l = mma(ones, pb[1], a[1].l);
+#pragma unroll
+  for (int jt = 0; jt < kVd; ++jt) a[1].o[jt] = mma(av[jt], pb[1], a[1].o[jt]);
 }
 
 // Direct global-to-LDS staging (global_load_lds_dwordx4).  One instruction
@@ -299,14 +313,18 @@ __device__ inline void step_scores(f32x4 (&s)[kRowTiles][2], const unsigned char
   for (int nr = 0; nr < kRowTiles; ++nr)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[nr][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 k[D / 32][2];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const u32x4 k = *(const u32x4*)(ks + 2048 * i + 512 * kt);
+    for (int kt = 0; kt < 2; ++kt) k[i][kt] = *(const u32x4*)(ks + 2048 * i + 512 * kt);
+  // Tile 0 first: its running max can then be taken while tile 1's products run.
 #pragma unroll
-      for (int nr = 0; nr < kRowTiles; ++nr) s[nr][kt] = mma(k, qb[nr][i], s[nr][kt]);
-    }
+  for (int nr = 0; nr < kRowTiles; ++nr)
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[nr][kt] = mma(k[i][kt], qb[nr][i], s[nr][kt]);
 }
 
 // The V^T operands of one step (A operands of the PV MFMAs).  Tile jt covers

@@ -74,6 +74,11 @@ def test_decode_plan(pa):
     plan = pa.decode_plan(16, 64, 8, 128, 16, 8192, kernel="mfma")
     assert plan.num_partitions > 1 and plan.partition_size % 32 == 0
     assert plan.num_partitions * plan.partition_size >= 8192
+    # the split aims at 512 work-groups (two per CU): 128 (sequence, KV head)
+    # pairs of 8,192 tokens take 4 partitions of 2,048
+    assert (plan.partition_size, plan.num_partitions) == (2048, 4)
+    # 512 pairs already fill both slots of every CU
+    assert pa.decode_plan(64, 64, 8, 128, 16, 8192, kernel="mfma").num_partitions == 1
     # 256 (sequence, head) pairs fill the GPU for the split kernel: no split
     assert pa.decode_plan(256, 64, 8, 128, 16, 951, kernel="mfma").num_partitions == 1
     # the matrix-core split kernel rounds partitions to whole 32-token steps

@@ -62,7 +62,7 @@ def parse():
                          "| layered_llama70b (8 layers of a layered pool per launch)")
     ap.add_argument("--rotate", type=int, default=4, help="KV pool copies cycled over steps")
     ap.add_argument("--partition", type=int, default=0, help="0 = library's choice")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "valu"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--fused-append", action="store_true",
                     help="append inside the decode launch (pa_decode_append)")
     ap.add_argument("--rank-in-kernel", action="store_true",
@@ -513,7 +513,7 @@ def main():
     lens = to_dev(w.seq_lens)
     k_new, v_new, slots = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping)
     fk, fv, fslots = (to_dev(a) for a in W.per_sequence_append(w))
-    fused = w.slot_mapping.shape[0] > 0 and args.fused_append and args.kernel != "stream"
+    fused = w.slot_mapping.shape[0] > 0 and args.fused_append
     pairs = to_dev(w.cow_pairs)
     out = torch.empty_like(q)
     plan = pa.decode_plan(w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size,
@@ -591,7 +591,7 @@ def main():
                                                         for n in w.seq_lens)) + 4 * w.num_seqs)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
     kernel_name = f"decode_{plan.kernel}_kernel" + (" (fused append)" if fused else "")
-    split_reduce = plan.kernel != "stream" and nparts > 1
+    split_reduce = nparts > 1
     if shared:
         kernel_name = "shared_prefix_kernel (prefix + tails) + prefix_merge_kernel"
         split_reduce = False
@@ -640,7 +640,7 @@ def main():
             "cow_pairs": int(w.cow_pairs.shape[0]),
             "kernel": plan.kernel,
             "partition_size": eff_p,
-            "num_partitions" if plan.kernel != "stream" else "workgroups": nparts,
+            "num_partitions": nparts,
             "pool_rotation": len(pools),
             "parallelism": "single GPU",
         },

@@ -18,9 +18,8 @@
  * call says otherwise: the group arrays of pa_decode_shared_prefix and every
  * block-manager argument are host memory, and pa_swap_blocks moves blocks to
  * and from pinned host memory.  The library allocates nothing and frees
- * nothing.  Its only state is a call counter that
- * tags the stream kernel's tickets and a cached compute-unit count per
- * device; every call is otherwise independent.
+ * nothing.  Its only state is a cached compute-unit count per device (used
+ * to size the shared-prefix split); every call is otherwise independent.
  *
  * One layer's cache.  `k_cache` and `v_cache` are each
  *     [num_blocks][kv_heads][block_size][head_dim]
@@ -72,12 +71,8 @@ typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 typedef enum pa_kernel {
   PA_KERNEL_AUTO = 0,   /* MFMA when it supports the shape, else VALU        */
   PA_KERNEL_VALU = 1,   /* vector-ALU split kernel: fp32 or bf16, G <= 8     */
-  PA_KERNEL_MFMA = 2,   /* matrix-core split kernel (+ reduce kernel)        */
-  PA_KERNEL_STREAM = 3  /* matrix-core persistent kernel: a fixed grid of
-                           work-groups shares the batch's work evenly and
-                           merges cut sequences in-kernel (measured slower
-                           than MFMA on MI355X; kept as an option).  MFMA and
-                           STREAM: bf16, head_dim 64/128, block_size 16..256,
+  PA_KERNEL_MFMA = 2    /* matrix-core split kernel (+ reduce kernel): bf16,
+                           head_dim 64/128, block_size 16..256,
                            num_heads/kv_heads <= 16                          */
 } pa_kernel;
 
@@ -101,7 +96,8 @@ pa_status pa_block_layout(int64_t tokens, int32_t block_size, int64_t* blocks, i
 /*
  * KV append: write the keys and values of `num_tokens` new tokens into the
  * cache slots named by `slot_mapping` ("How PagedAttention works", section
- * "A strong answer": a sequence's cache grows by one token per decode step).
+ * "A strong answer": every decode step adds the new token's K/V to the
+ * sequence's blocks).
  *
  *   k_new, v_new   [num_tokens][kv_heads][head_dim], dtype
  *   k_cache,       [num_blocks][kv_heads][block_size][head_dim], written in place
@@ -132,19 +128,17 @@ pa_status pa_kv_append(const void* k_new, const void* v_new, void* k_cache, void
  * result per partition (running max, running sum, unnormalised output) in the
  * workspace and a reduce kernel merges them.
  *   partition_size > 0 : used as given by VALU; rounded up to a multiple of
- *                        32 tokens by MFMA;
+ *                        32 tokens by MFMA; in both cases capped at
+ *                        max_seq_len (rounded the same way), so any value up
+ *                        to INT32_MAX is accepted and a huge one means "do
+ *                        not split";
  *   partition_size = 0 : chosen from num_seqs*kv_heads and max_seq_len (no
  *                        split when there are enough (sequence, head) pairs
  *                        to fill the GPU).
  *   workspace = num_seqs*num_heads*num_partitions*(head_dim+2)*4 bytes when
  *   num_partitions > 1, else 0.  More than 16384 partitions per sequence is
- *   PA_ERR_UNSUPPORTED.
- * Stream kernel (STREAM): partition_size is ignored; *eff_partition_size = 0
- * and *num_partitions = the number of work-groups (2 per compute unit of the
- * current device, 256 compute units assumed when no device is visible).
- *   workspace = 8*kv_heads*num_seqs (tickets) + 2*num_workgroups*num_heads/
- *   kv_heads*(head_dim+2)*4 bytes (partials), 16-byte aligned pieces.  It
- *   needs no initialising: tickets carry a per-call tag.
+ *   PA_ERR_UNSUPPORTED; max_seq_len within 32 of INT32_MAX is
+ *   PA_ERR_INVALID_ARG.
  * Two calls in flight at once must not share a workspace.
  */
 pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim,
@@ -244,13 +238,16 @@ pa_status pa_decode_ordered(void* out, const void* q, const void* k_cache, const
  *   seq_lens       lengths AFTER the append; when slot_mapping[s] >= 0 the new
  *                  token is position seq_lens[s] - 1, and slot_mapping[s] must
  *                  be that position's slot under the sequence's block table
- * The decode reads the new token from k_new/v_new, never from the slot being
- * written, so no work-group reads what another writes.  The slot's block must
- * not be read by any other sequence in the same call (copy-on-write first).
- * Other arguments, errors and shapes as pa_decode_ex; kernel PA_KERNEL_STREAM
- * gives PA_ERR_UNSUPPORTED.  On the 70B-shaped batch one launch measured a
- * little slower than pa_kv_append + pa_decode (the owning work-group folds
- * the new token in serially after its step loop).
+ * The new token's score and value come from k_new/v_new.  The matrix-core
+ * kernel's loads of the last tile may still read the slot being written
+ * (by another work-group of the same launch), but that position is masked
+ * out of the step math before its value is used, so the result never
+ * depends on what the read returns.  The slot's block must not be read by
+ * any other sequence in the same call (copy-on-write first).
+ * Other arguments, errors and shapes as pa_decode_ex.  On the 70B-shaped
+ * batch one launch measured a little slower than pa_kv_append + pa_decode
+ * (the owning work-group folds the new token in serially after its step
+ * loop).
  */
 pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
                            const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -283,8 +280,9 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
  *                        prefix is group_prefix_blocks[g] * block_size tokens
  *   num_groups           0 .. PA_MAX_PREFIX_GROUPS (0: plain decode)
  *   prefix_partition_size  keys per prefix-kernel partition (rounded up to a
- *                        multiple of 32); 0 = the library's choice (about two
- *                        work-groups per compute unit)
+ *                        multiple of 32 and capped at the longest prefix, so
+ *                        INT32_MAX means "do not split"); 0 = the library's
+ *                        choice (about one work-group per compute unit)
  *   partition_size       tail partitions, as in pa_decode (0 = default)
  *   workspace            device, >= pa_decode_shared_prefix_workspace_bytes()
  *                        with the same arguments, 16-byte aligned

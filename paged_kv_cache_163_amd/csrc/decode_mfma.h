@@ -216,9 +216,12 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
   // Shared-prefix decode: positions before `pfx` belong to the prefix kernel.
   int pfx = 0;
   if constexpr (M == kModeTail) pfx = shared_prefix_tokens(p.prefix, w.seq);
-  const int pstart = pfx + w.part * p.partition_size;
-  if (pstart >= len) return;
-  const int pend = min(len, pstart + p.partition_size);
+  // w.part * partition_size < max_seq_len by the plan; the sum with the
+  // prefix is formed in 64 bits
+  const int64_t pstart64 = (int64_t)pfx + (int64_t)w.part * p.partition_size;
+  if (pstart64 >= len) return;
+  const int pstart = (int)pstart64;
+  const int pend = range_end(pstart, p.partition_size, len);
   const int nparts = ceil_div_i(len - pfx, p.partition_size);
   // Fused append: the partition that holds the new token (position len - 1,
   // so the last one) masks it out of the step math and folds it in from the

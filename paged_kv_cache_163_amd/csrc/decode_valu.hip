@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
   }
   const int pstart = w.part * p.partition_size;
   if (pstart >= len) return;
-  const int pend = min(len, pstart + p.partition_size);
+  const int pend = range_end(pstart, p.partition_size, len);
   const int nparts = ceil_div_i(len, p.partition_size);
 
   float qf[G][kVec];

@@ -1,5 +1,6 @@
 // One wave's 32-token step of paged decode attention on the gfx950 matrix
-// cores, shared by the split-partition and the stream decode kernels.
+// cores, shared by the split-partition decode work-group and the shared-prefix
+// tail work-groups.
 //
 // A step is two 16-token tiles.  Block sizes are powers of two >= 16, so a
 // tile never straddles two physical blocks and costs one block-table read

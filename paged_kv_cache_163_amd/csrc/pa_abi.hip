@@ -2,13 +2,10 @@
 // planning (kernel, partition size, grid, workspace) and kernel dispatch.
 // Every check on host-side arguments runs before anything is launched; the
 // only HIP calls before a launch are the device and compute-unit queries of
-// the stream kernel's plan and the pointer-attribute queries of the block
-// swap.
+// the shared-prefix plan and the pointer-attribute queries of the block swap.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
-#include <time.h>
-#include <unistd.h>
 
 #include <atomic>
 
@@ -17,7 +14,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 // Work-groups a decode launch should offer before sequences are split: the
 // two resident four-wave work-groups per compute unit of a 256-CU MI355X.
 // Measured on 16 sequences x 8,192 tokens x 8 KV heads: 89 us at 2,048-token
@@ -26,7 +23,6 @@ constexpr int32_t kAbiVersion = 1;
 constexpr int64_t kTargetWorkgroups = 512;
 constexpr int32_t kMfmaStep = 32;  // tokens per MFMA-kernel step
 constexpr int64_t kMaxPartitions = 16384;  // partitions per sequence (split kernels)
-constexpr int32_t kStreamWgsPerCu = 2;   // resident 4-wave work-groups per CU
 constexpr int32_t kDefaultCus = 256;     // MI355X, used when no device is visible
 constexpr int kMaxDevices = 64;
 
@@ -50,17 +46,6 @@ int32_t device_cus() {
   return cus;
 }
 
-// Per-call tag of the stream kernel's tickets; starts at a per-process value
-// so tickets left in recycled memory by another process do not match.
-uint32_t next_epoch() {
-  static std::atomic<uint32_t> counter{(uint32_t)time(nullptr) * 2654435761u ^
-                                       ((uint32_t)getpid() << 16)};
-  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed);
-  return e;
-}
-
-size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
-
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 int32_t log2i(int64_t v) {
@@ -74,10 +59,9 @@ int32_t elem_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
 bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
 
 struct Plan {
-  int32_t kernel;      // PA_KERNEL_VALU, PA_KERNEL_MFMA or PA_KERNEL_STREAM
-  int32_t partition;   // tokens per partition (split kernels), 0 (stream)
-  int32_t partitions;  // grid extent along partitions (split), work-groups (stream)
-  size_t tickets;      // stream: bytes of the ticket array at the workspace start
+  int32_t kernel;      // PA_KERNEL_VALU or PA_KERNEL_MFMA
+  int32_t partition;   // tokens per partition
+  int32_t partitions;  // grid extent along partitions
   size_t workspace;    // bytes
 };
 
@@ -100,21 +84,14 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32
       head_dim <= 0 || block_size <= 0 || max_seq_len < 0 || partition_size < 0 ||
       !dtype_ok(dtype))
     return PA_ERR_INVALID_ARG;
-  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA &&
-      kernel != PA_KERNEL_STREAM)
+  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
     return PA_ERR_INVALID_ARG;
   if (!pow2(block_size) || block_size > 256) return PA_ERR_UNSUPPORTED;
   const int32_t group = num_heads / kv_heads;
   const bool mfma = mfma_supports(dtype, head_dim, group, block_size);
   const bool valu = valu_supports(dtype, head_dim, group, block_size);
-  // The stream kernel indexes its work in int32 steps of 32 tokens.
-  const bool stream_fits =
-      (int64_t)kv_heads * num_seqs * ceil_div(max_seq_len, kMfmaStep) < (int64_t)INT32_MAX;
   int32_t chosen;
-  if (kernel == PA_KERNEL_STREAM) {
-    if (!mfma || !stream_fits) return PA_ERR_UNSUPPORTED;
-    chosen = kernel;
-  } else if (kernel == PA_KERNEL_MFMA) {
+  if (kernel == PA_KERNEL_MFMA) {
     if (!mfma) return PA_ERR_UNSUPPORTED;
     chosen = kernel;
   } else if (kernel == PA_KERNEL_VALU) {
@@ -124,16 +101,12 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32
     if (!mfma && !valu) return PA_ERR_UNSUPPORTED;
     chosen = mfma ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
   }
-  if (chosen == PA_KERNEL_STREAM) {
-    const int64_t wgs = (int64_t)kStreamWgsPerCu * device_cus();
-    plan->kernel = chosen;
-    plan->partition = 0;
-    plan->partitions = (int32_t)wgs;
-    plan->tickets = align16((size_t)kv_heads * num_seqs * 8);
-    plan->workspace = plan->tickets + (size_t)2 * wgs * group * (head_dim + 2) * 4;
-    return PA_OK;
-  }
   const int64_t granule = chosen == PA_KERNEL_MFMA ? kMfmaStep : 1;
+  // A partition never needs to be longer than the longest sequence, so a
+  // requested size is capped there (a huge request such as INT32_MAX means
+  // "do not split"); every later sum of a start and a partition size then
+  // stays within int32 on the device.
+  const int64_t whole = round_up(max_seq_len > 0 ? max_seq_len : 1, granule);
   int64_t part;
   if (partition_size > 0) {
     part = round_up(partition_size, granule);
@@ -147,7 +120,8 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32
     if (part < 256) part = 256;
     part = round_up(part, chosen == PA_KERNEL_MFMA ? kMfmaStep : 16);
   }
-  if (part > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (part > whole) part = whole;
+  if (part > INT32_MAX - kMfmaStep) return PA_ERR_INVALID_ARG;
   const int64_t parts = max_seq_len > 0 ? ceil_div(max_seq_len, part) : 1;
   if (parts > kMaxPartitions) return PA_ERR_UNSUPPORTED;  // reduce kernel's LDS weights
   const int64_t grid = parts * (int64_t)num_seqs * kv_heads;
@@ -155,7 +129,6 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32
   plan->kernel = chosen;
   plan->partition = (int32_t)part;
   plan->partitions = (int32_t)parts;
-  plan->tickets = 0;
   plan->workspace = parts > 1 ? (size_t)num_seqs * num_heads * parts * (head_dim + 2) * 4 : 0;
   return PA_OK;
 }
@@ -246,6 +219,11 @@ pa_status shared_prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_hea
     const int64_t splits = base >= target ? 1 : target / base;
     part = round_up(ceil_div(max_tokens, splits), kMfmaStep);
   }
+  // no prefix partition is longer than the longest prefix (a huge request
+  // means "do not split"), which keeps the device's int32 sums in range
+  const int64_t whole = round_up(max_tokens, kMfmaStep);
+  if (part > whole) part = whole;
+  if (part > INT32_MAX - kMfmaStep) return PA_ERR_INVALID_ARG;
   const int64_t parts = ceil_div(max_tokens, part);
   const int64_t slots = parts + tail.partitions;
   if (slots > kMaxPartitions || (int64_t)group * slots * 4 > 64 * 1024) return PA_ERR_UNSUPPORTED;
@@ -309,7 +287,6 @@ static pa_status decode_impl(void* out, const void* q, const void* k_cache, cons
     return PA_ERR_INVALID_ARG;
   const bool fused = new_slots != nullptr;
   if (fused) {
-    if (plan.kernel == PA_KERNEL_STREAM) return PA_ERR_UNSUPPORTED;
     if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(new_slots, 8))
       return PA_ERR_INVALID_ARG;
   }
@@ -329,12 +306,7 @@ static pa_status decode_impl(void* out, const void* q, const void* k_cache, cons
     p.k_cache_w = (void*)k_cache;
     p.v_cache_w = (void*)v_cache;
   }
-  if (plan.kernel == PA_KERNEL_STREAM) {
-    p.tickets = (uint64_t*)workspace;
-    p.partials = (float*)((char*)workspace + plan.tickets);
-    p.num_workgroups = plan.partitions;
-    p.epoch = next_epoch();
-  } else if (plan.workspace > 0) {
+  if (plan.workspace > 0) {
     const size_t per_layer_o = (size_t)num_seqs * num_heads * plan.partitions * head_dim;
     p.ws_o = (float*)workspace;
     p.ws_ml = p.ws_o + per_layer_o * (lay != nullptr ? lay->layers : 1);
@@ -365,8 +337,6 @@ static pa_status decode_impl(void* out, const void* q, const void* k_cache, cons
 
   const hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dtype == PA_BF16;
-  if (plan.kernel == PA_KERNEL_STREAM)
-    return from_hip(pa::launch_decode_stream(p, head_dim, s));
   hipError_t e = plan.kernel == PA_KERNEL_MFMA ? pa::launch_decode_mfma(p, head_dim, s)
                                                : pa::launch_decode_valu(p, bf16, head_dim, s);
   if (e != hipSuccess) return PA_ERR_HIP;

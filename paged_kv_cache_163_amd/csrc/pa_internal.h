@@ -56,10 +56,6 @@ struct DecodeParams {
   const int64_t* new_slots;     // fused append: [B] cache slot of each new token (< 0: none)
   void* k_cache_w;              // fused append: writable views of the caches
   void* v_cache_w;
-  uint64_t* tickets;            // stream kernel: [Hkv][B] epoch-tagged arrival counts
-  float* partials;              // stream kernel: [num_workgroups][2][G*(D+2)]
-  int32_t num_workgroups;       // stream kernel grid
-  uint32_t epoch;               // stream kernel: unique per call
   int32_t num_seqs;
   int32_t num_heads;
   int32_t kv_heads;
@@ -135,7 +131,15 @@ __device__ inline WorkItem decode_work_item(const DecodeParams& p, int wg) {
   return w;
 }
 
-__device__ inline int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+// ceil(a / b) for b > 0 without forming a + b - 1 (partition sizes may be
+// close to INT32_MAX); 0 for a <= 0.
+__device__ inline int ceil_div_i(int a, int b) { return a <= 0 ? 0 : (a - 1) / b + 1; }
+
+// End of the range of at most `size` positions starting at `start`, cut at
+// `limit` (start < limit), without forming start + size.
+__device__ inline int range_end(int start, int size, int limit) {
+  return limit - start <= size ? limit : start + size;
+}
 
 // A sequence length the grid and the table can serve.
 __device__ inline bool seq_len_ok(const DecodeParams& p, int len) {
@@ -235,10 +239,6 @@ hipError_t launch_decode_valu(const DecodeParams& p, bool is_bf16, int head_dim,
 // bf16 only; head_dim in {64, 128}; block_size >= 16; group <= 16;
 // partition_size a multiple of 32.
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream);
-
-// Persistent load-balanced kernel: bf16; head_dim in {64, 128}; block_size
-// >= 16; group <= 16; grid = num_workgroups.
-hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, hipStream_t stream);
 
 // Merges the per-partition partials of sequences with more than one partition.
 hipError_t launch_decode_reduce(const DecodeParams& p, bool is_bf16, int head_dim,

@@ -57,7 +57,7 @@ __device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x,
   const int head = combo % p.kv_heads;
   const int kp = combo / p.kv_heads;
   const int kstart = kp * pg.partition;
-  const int kend_wg = min(tokens, kstart + pg.partition);
+  const int kend_wg = range_end(kstart, pg.partition, tokens);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

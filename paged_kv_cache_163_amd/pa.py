@@ -39,7 +39,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_SPACE = 0, 1, 2, 3, 4
 PA_F32, PA_BF16 = 0, 1
-KERNELS = {"auto": 0, "valu": 1, "mfma": 2, "stream": 3}
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -206,9 +206,9 @@ def copy_blocks(k_cache, v_cache, block_mapping, stream=None) -> None:
 
 
 class Plan(NamedTuple):
-    kernel: str            # "valu", "mfma" (split partitions) or "stream"
-    partition_size: int    # tokens per partition (0 for "stream")
-    num_partitions: int    # partitions (split kernels) or work-groups ("stream")
+    kernel: str            # "valu" or "mfma" (split partitions)
+    partition_size: int    # tokens per partition
+    num_partitions: int    # partitions per sequence (grid extent)
     workspace_bytes: int
 
 

@@ -18,7 +18,7 @@
 
 int main(void) {
   int64_t blocks = -1, unused = -1;
-  CHECK(1, pa_abi_version() == 1);
+  CHECK(1, pa_abi_version() == 2);
   CHECK(2, pa_block_layout(10, 4, &blocks, &unused) == PA_OK && blocks == 3 && unused == 2);
   CHECK(3, pa_block_layout(-1, 4, &blocks, &unused) == PA_ERR_INVALID_ARG);
   CHECK(4, strcmp(pa_status_string(PA_OK), "ok") == 0);

@@ -46,7 +46,7 @@ def pa(built_lib):
 
 def test_binding_export_list_matches_header(pa):
     assert sorted(pa.EXPORTED) == declared_functions()
-    assert pa.abi_version() == 1
+    assert pa.abi_version() == 2
 
 
 def test_block_layout_matches_oracle(pa):
@@ -62,12 +62,6 @@ def test_decode_plan(pa):
     import torch
     # bf16 batches go to the split matrix-core kernel by default
     assert pa.decode_plan(256, 64, 8, 128, 16, 951).kernel == "mfma"
-    # the persistent stream kernel: 2 work-groups per CU (256 CUs assumed
-    # without a device), tickets + 2 partial slots each
-    plan = pa.decode_plan(256, 64, 8, 128, 16, 951, kernel="stream")
-    assert plan.kernel == "stream" and plan.partition_size == 0
-    nwg = plan.num_partitions
-    assert nwg >= 2 and plan.workspace_bytes == 256 * 8 * 8 + 2 * nwg * 8 * 130 * 4
     # an explicit partition size selects the split kernel and its workspace
     plan = pa.decode_plan(16, 64, 8, 128, 16, 8192, partition_size=512)
     assert plan == ("mfma", 512, 16, 16 * 64 * 16 * 130 * 4)
@@ -88,16 +82,53 @@ def test_decode_plan(pa):
     assert pa.decode_plan(4, 8, 2, 64, 4, 100, partition_size=8, dtype=torch.float32) == \
         ("valu", 8, 13, 4 * 8 * 13 * 66 * 4)
     assert pa.decode_plan(4, 8, 2, 64, 4, 100, dtype=torch.float32).kernel == "valu"
-    for k in ("mfma", "stream"):
-        with pytest.raises(NotImplementedError):
-            pa.decode_plan(4, 8, 2, 64, 4, 100, dtype=torch.float32, kernel=k)
+    with pytest.raises(NotImplementedError):
+        pa.decode_plan(4, 8, 2, 64, 4, 100, dtype=torch.float32, kernel="mfma")
     with pytest.raises(NotImplementedError):
         pa.decode_plan(4, 8, 2, 96, 16, 100)           # head_dim 96 not instantiated
     with pytest.raises(ValueError):
         pa.decode_plan(4, 9, 2, 64, 16, 100)           # 9 query heads over 2 KV heads
-    # the stream kernel counts steps in int32
-    with pytest.raises(NotImplementedError):
-        pa.decode_plan(65536, 64, 8, 128, 16, 1 << 20, kernel="stream")
+    # no kernel choice beyond the two split kernels
+    with pytest.raises(KeyError):
+        pa.decode_plan(4, 8, 2, 64, 16, 100, kernel="stream")
+
+
+def test_decode_plan_caps_partition_at_the_longest_sequence(pa):
+    """A partition size up to INT32_MAX is accepted and means "do not split":
+    the plan caps it at max_seq_len rounded to the kernel's granule, so the
+    device's start + size sums stay inside int32."""
+    import torch
+    big = 2**31 - 1
+    assert pa.decode_plan(16, 64, 8, 128, 16, 8192, partition_size=big) == \
+        ("mfma", 8192, 1, 0)
+    assert pa.decode_plan(4, 8, 2, 64, 16, 100, partition_size=big) == ("mfma", 128, 1, 0)
+    assert pa.decode_plan(4, 8, 2, 64, 4, 100, partition_size=big, dtype=torch.float32) == \
+        ("valu", 100, 1, 0)
+    # one below the cap still splits
+    assert pa.decode_plan(16, 64, 8, 128, 16, 8192, partition_size=8160).num_partitions == 2
+    # the longest sequences the int32 grid arithmetic takes
+    plan = pa.decode_plan(1, 8, 8, 128, 16, big - 64, partition_size=big)
+    assert plan.num_partitions == 1 and plan.partition_size == big - 63
+    with pytest.raises(ValueError):
+        pa.decode_plan(1, 8, 8, 128, 16, big, partition_size=big)
+
+
+def test_shared_prefix_plan_caps_prefix_partition(pa):
+    """prefix_partition_size = INT32_MAX is one prefix partition: the workspace
+    holds one prefix slot and the tail slots, never a wrapped int32 size."""
+    B, Hq, Hkv, D, bs = 8, 64, 8, 128, 16
+    maxlen, maxblk = 3000, 200
+    groups = ([0, B], [125])
+    tail = pa.decode_plan(B, Hq, Hkv, D, bs, maxlen, partition_size=512, kernel="mfma")
+    ws = pa.shared_prefix_workspace_bytes(B, Hq, Hkv, D, bs, maxlen, maxblk, *groups,
+                                          prefix_partition_size=2**31 - 1, partition_size=512)
+    assert ws == B * Hq * (1 + tail.num_partitions) * (D + 2) * 4
+    ws2 = pa.shared_prefix_workspace_bytes(B, Hq, Hkv, D, bs, maxlen, maxblk, *groups,
+                                           prefix_partition_size=2000, partition_size=512)
+    assert ws2 == ws
+    ws4 = pa.shared_prefix_workspace_bytes(B, Hq, Hkv, D, bs, maxlen, maxblk, *groups,
+                                           prefix_partition_size=512, partition_size=512)
+    assert ws4 == B * Hq * (4 + tail.num_partitions) * (D + 2) * 4
 
 
 def test_host_validation_rejects_before_launch(built_lib):
@@ -132,12 +163,11 @@ def test_host_validation_rejects_before_launch(built_lib):
     assert call(d=96) == UNSUPPORTED
     assert call(bs=12) == UNSUPPORTED                 # not a power of two
     assert call(dt=0, kern=2) == UNSUPPORTED          # fp32 has no matrix-core kernel
-    assert call(dt=0, kern=3) == UNSUPPORTED
+    assert call(kern=3) == INVALID                    # no kernel 3 (the removed stream kernel)
     # split needed (16 long sequences at P=512) but no workspace given
     assert call(B=16, maxlen=8192, maxblk=512, part=512) == INVALID
-    # the stream kernel always needs its workspace
-    assert call(kern=3) == INVALID
-    assert call(kern=3, ws=vp(4096), wsb=16) == INVALID   # too small
+    # a split with a workspace that is too small
+    assert call(B=16, maxlen=8192, maxblk=512, part=512, ws=vp(4096), wsb=16) == INVALID
     assert call(B=0) == 0                             # nothing to do, nothing launched
 
     app = lib.pa_kv_append
@@ -153,10 +183,10 @@ def test_host_validation_rejects_before_launch(built_lib):
     assert fa(fake, fake, fake, fake, fake, fake, none, fake, i32(4), fake, i32(16), i32(2),
               i32(8), i32(2), i32(64), i32(16), i32(8), ctypes.c_float(0.1), i32(0), fake,
               ctypes.c_size_t(1 << 20), i32(1), i32(0), none) == INVALID
-    # fused call on the stream kernel
+    # fused call naming no kernel the library has
     assert fa(fake, fake, fake, fake, fake, fake, fake, fake, i32(4), fake, i32(16), i32(2),
               i32(8), i32(2), i32(64), i32(16), i32(8), ctypes.c_float(0.1), i32(0), fake,
-              ctypes.c_size_t(1 << 26), i32(1), i32(3), none) == UNSUPPORTED
+              ctypes.c_size_t(1 << 26), i32(1), i32(3), none) == INVALID
     cp = lib.pa_copy_blocks
     cp.restype = ctypes.c_int32
     assert cp(fake, fake, fake, i32(-2), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID

@@ -88,7 +88,7 @@ def test_pool_beyond_4gib_every_call(pa):
     assert bool(torch.isnan(k[:HIGH]).all())                    # nothing written below
     ref = oracle.paged_decode(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale, w.block_size)
     lens, q = dev(w.seq_lens), dev(w.q)
-    for kernel, part in (("mfma", 0), ("mfma", 64), ("valu", 0), ("stream", 0)):
+    for kernel, part in (("mfma", 0), ("mfma", 64), ("valu", 0)):
         out = pa.decode(q, k, v, bt, lens, w.scale, max_seq_len=w.max_seq_len, kernel=kernel,
                         partition_size=part)
         torch.cuda.synchronize()
@@ -119,7 +119,7 @@ def test_longest_sequence_up_to_the_partition_limit(pa):
     ref = oracle.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.scale, 16)
     d = dict(q=dev(w.q), k=dev(w.k_cache), v=dev(w.v_cache), bt=dev(w.block_tables),
              lens=dev(w.seq_lens))
-    cases = (("mfma", 0), ("mfma", 32), ("valu", 16), ("stream", 0))
+    cases = (("mfma", 0), ("mfma", 32), ("valu", 16))
     for kernel, part in cases:
         plan = pa.decode_plan(2, 8, 1, 128, 16, L, part, torch.bfloat16, kernel)
         if kernel == "valu":

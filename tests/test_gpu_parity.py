@@ -6,10 +6,10 @@ decode outputs are within max |gpu - ref| <= 1e-5 for float32 inputs and
 accumulation), both against the float64 oracle on the same (bf16-rounded)
 inputs.
 
-Small cases compare every output element; the full-size workloads run in the
-launch configuration the benchmark times and compare a seeded sample of
-sequences (all heads, all head-dim elements) that the oracle computes one by
-one, plus whole-pool byte comparisons for the writes.
+Small cases compare every output element.  The full-size workloads run in the
+launch configuration the benchmark times and compare every sequence (all
+heads, all head-dim elements) with the oracle, plus whole-pool byte
+comparisons for the writes.
 """
 
 import numpy as np
@@ -107,14 +107,6 @@ def gpu_step(pa, d, w):
     torch.cuda.synchronize()
 
 
-def sample_seqs(w, n, seed=0):
-    rng = np.random.default_rng(seed + 1000)
-    B = w.num_seqs
-    pick = set(rng.choice(B, size=min(n, B), replace=False).tolist())
-    pick |= {int(np.argmin(w.seq_lens)), int(np.argmax(w.seq_lens))}
-    return sorted(pick)
-
-
 def small_bf16(lens, block_size, head_dim, num_heads, kv_heads, seed=0):
     nb = sum(-(-max(n, 1) // block_size) for n in lens) + 8
     return W.build_private("small", lens, dtype="bf16", num_heads=num_heads, kv_heads=kv_heads,
@@ -181,8 +173,21 @@ def test_ragged_bf16_both_kernels(pa, block_size, head_dim):
                 out = decode(pa, d, w, partition_size=partition, kernel=kernel)
                 assert_close(as_f64(out), ref, "bf16",
                              f"b={block_size} d={head_dim} G={hq // hkv} {kernel} P={partition}")
-        out = decode(pa, d, w, kernel="stream")
-        assert_close(as_f64(out), ref, "bf16", f"b={block_size} d={head_dim} G={hq // hkv} stream")
+
+
+def test_partition_size_int32_max_is_no_split(pa):
+    """partition_size = INT32_MAX is accepted and means one partition per
+    sequence (capped at max_seq_len), for both kernels and the fused step."""
+    big = 2**31 - 1
+    w = small_bf16(RAGGED, 16, 128, 64, 8, seed=77)
+    d = upload(w)
+    ref = oracle_decode(w)
+    for kernel in ("mfma", "valu"):
+        plan = pa.decode_plan(w.num_seqs, 64, 8, 128, 16, w.max_seq_len, big, torch.bfloat16,
+                              kernel)
+        assert plan.num_partitions == 1
+        out = decode(pa, d, w, partition_size=big, kernel=kernel)
+        assert_close(as_f64(out), ref, "bf16", f"{kernel} P=INT32_MAX")
 
 
 @pytest.mark.parametrize("hq,hkv", [(16, 16), (16, 4), (64, 4)])
@@ -190,39 +195,9 @@ def test_group_sizes_mfma(pa, hq, hkv):
     """G = 1, 4 and 16 query heads per KV head on the matrix-core kernels."""
     w = small_bf16([3, 40, 129, 700], 16, 128, hq, hkv, seed=hq * 7 + hkv)
     d = upload(w)
-    for kernel in ("mfma", "stream"):
-        out = decode(pa, d, w, kernel=kernel, partition_size=0)
-        assert_close(as_f64(out), oracle_decode(w), "bf16", f"G={hq // hkv} {kernel}")
-
-
-@pytest.mark.parametrize("lens", [
-    [5],                        # fewer steps (8) than work-groups
-    [8192],                     # one unit per head cut across many work-groups
-    [1] * 300 + [4000],         # hundreds of one-step units, then a long one
-    [33, 0, 64, 0, 1, 2500],    # zero-length sequences inside the step space
-], ids=["tiny", "one-long", "many-short", "with-empty"])
-def test_stream_work_split(pa, lens):
-    """The stream kernel's share boundaries: cut units merged through tickets."""
-    w = small_bf16([max(n, 1) for n in lens], 16, 128, 64, 8, seed=len(lens))
-    lens_arr = np.asarray(lens, dtype=np.int32)
-    d = upload(w)
-    d["lens"] = dev(lens_arr)
-    ref = oracle.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, lens_arr, w.scale, 16)
-    plan = pa.decode_plan(w.num_seqs, 64, 8, 128, 16, int(lens_arr.max()), kernel="stream")
-    assert plan.kernel == "stream"
-    # a workspace full of garbage (tickets from no call at all) must not matter
-    ws = torch.randint(0, 255, (plan.workspace_bytes,), dtype=torch.uint8, device=DEV)
-    outs = []
-    for _ in range(3):
-        o = pa.decode(d["q"], d["k"], d["v"], d["bt"], d["lens"], w.scale,
-                      max_seq_len=int(lens_arr.max()), workspace=ws, kernel="stream")
-        torch.cuda.synchronize()
-        outs.append(o.clone())
-    got = as_f64(outs[0])
-    assert_close(got[lens_arr > 0], ref[lens_arr > 0], "bf16", f"stream {lens[:3]}")
-    assert np.all(got[lens_arr == 0] == 0.0)
-    # repeated calls (new ticket tag each time) give the same bytes
-    assert all(torch.equal(outs[0].view(torch.int16), o.view(torch.int16)) for o in outs[1:])
+    for partition in (32, 0):
+        out = decode(pa, d, w, kernel="mfma", partition_size=partition)
+        assert_close(as_f64(out), oracle_decode(w), "bf16", f"G={hq // hkv} P={partition}")
 
 
 def test_edge_lengths_and_bad_contents(pa):
@@ -231,7 +206,7 @@ def test_edge_lengths_and_bad_contents(pa):
     lens = [0, 5, 40, 33]
     w = small_bf16([max(n, 1) for n in lens], 16, 128, 64, 8, seed=3)
     lens_arr = np.asarray(lens, dtype=np.int32)
-    for kernel in ("stream", "mfma", "valu"):
+    for kernel in ("mfma", "valu"):
         d = upload(w)
         d["lens"] = dev(lens_arr)
         bt = w.block_tables.copy()
@@ -284,39 +259,46 @@ def test_copy_blocks_bit_exact_and_skips_bad_pairs(pa):
 # full-size workloads (launch configuration of the benchmark: partition 0)
 # --------------------------------------------------------------------------
 
-def _full_step_and_decode(pa, w, nsample=24, **kw):
+def _full_step_and_decode(pa, w, **kw):
+    """The benchmark's step (copy-on-write copies, append) on the whole
+    workload, the pools compared byte for byte, then pa_decode compared with
+    the oracle on every sequence.  Returns the uploaded state, the output, the
+    oracle's pools after the step and the oracle's output."""
     d = upload(w)
     gpu_step(pa, d, w)
     kc, vc = oracle_step(w)
     assert np.array_equal(host(d["k"]), kc), "K pool differs after the step"
     assert np.array_equal(host(d["v"]), vc), "V pool differs after the step"
     out = decode(pa, d, w, **kw)
-    seqs = sample_seqs(w, nsample)
-    ref = oracle_decode(w, kc, vc, seqs=seqs)
-    assert_close(as_f64(out)[seqs], ref, w.dtype, w.name)
-    return d, out, kc, vc
+    ref = oracle_decode(w, kc, vc)
+    assert_close(as_f64(out), ref, w.dtype, w.name)
+    return d, out, kc, vc, ref
 
 
 def test_llama70b_full(pa):
     w = W.llama70b()
-    d, out, kc, vc = _full_step_and_decode(pa, w)
+    d, out, kc, vc, ref = _full_step_and_decode(pa, w)
     # deterministic: the same call gives the same bytes
     again = decode(pa, d, w)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
-    # the stream and vector-ALU kernels agree with the oracle too
-    seqs = sample_seqs(w, 8, seed=1)
-    for kernel in ("stream", "valu"):
-        o = decode(pa, d, w, kernel=kernel)
-        assert_close(as_f64(o)[seqs], oracle_decode(w, kc, vc, seqs=seqs), "bf16",
-                     f"llama70b {kernel}")
+    # the benchmark's own launch: pa_decode_ordered with the batch's
+    # longest-first order at the library's plan, every sequence
+    order = pa.longest_first(d["lens"])
+    plan = pa.decode_plan(w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size,
+                          w.max_seq_len, 0, torch.bfloat16, "auto")
+    assert plan.kernel == "mfma" and plan.num_partitions == 1
+    o = pa.decode_ordered(d["q"], d["k"], d["v"], d["bt"], d["lens"], order, w.scale,
+                          max_seq_len=w.max_seq_len)
+    torch.cuda.synchronize()
+    assert_close(as_f64(o), ref, "bf16", "llama70b, decode_ordered longest-first")
+    # the vector-ALU kernel agrees with the oracle too
+    o = decode(pa, d, w, kernel="valu")
+    assert_close(as_f64(o), ref, "bf16", "llama70b valu")
 
 
 def test_shared_prefix_full(pa):
     w = W.shared_prefix()
-    d, out, kc, vc = _full_step_and_decode(pa, w, nsample=8)
-    beams = list(range(200, 216))
-    ref = oracle_decode(w, kc, vc, seqs=beams + [w.meta["parent"]])
-    assert_close(as_f64(out)[beams + [w.meta["parent"]]], ref, "bf16", "beams")
+    d, out, kc, vc, _ = _full_step_and_decode(pa, w)
     # the parent's block and the prefix blocks were not touched by the beams' writes
     parent_last = int(w.cow_pairs[0, 0])
     keep = [parent_last] + list(w.meta["shared_blocks"])
@@ -347,9 +329,7 @@ def test_long_context_full(pa):
         o = decode(pa, d, w, partition_size=partition)
         assert_close(as_f64(o), ref, "bf16", f"long context P={partition}")
         outs[partition] = as_f64(o)
-    o = decode(pa, d, w, kernel="stream")
-    assert_close(as_f64(o), ref, "bf16", "long context stream")
-    # the partition size and the kernel change rounding only
+    # the partition size changes rounding only
     assert np.max(np.abs(outs[512] - outs[8192])) < 1e-2
     assert np.max(np.abs(outs[0] - outs[8192])) < 1e-2
 
@@ -357,7 +337,7 @@ def test_long_context_full(pa):
 @pytest.mark.parametrize("block_size,head_dim", W.SWEEP_CELLS)
 def test_sweep_full(pa, block_size, head_dim):
     w = W.sweep(block_size, head_dim)
-    _full_step_and_decode(pa, w, nsample=16)
+    _full_step_and_decode(pa, w)
 
 
 # --------------------------------------------------------------------------
@@ -385,7 +365,8 @@ def test_fused_append_decode(pa, kernel, block_size, head_dim):
     kc, vc = oracle_step(w)
     ref = oracle_decode(w, kc, vc)
     k, v, slots = W.per_sequence_append(w)
-    for partition in (32, 64, 0):        # P=32 leaves some new tokens alone in a partition
+    # P=32 leaves some new tokens alone in a partition; INT32_MAX is no split
+    for partition in (32, 64, 0, 2**31 - 1):
         d = upload(w)
         out = pa.decode_append(d["q"], d["k"], d["v"], dev(k), dev(v), dev(slots), d["bt"],
                                d["lens"], w.scale, max_seq_len=w.max_seq_len,
@@ -420,11 +401,7 @@ def test_fused_append_decode_full_size(pa):
                            w.scale, max_seq_len=w.max_seq_len)
     torch.cuda.synchronize()
     assert np.array_equal(host(d["k"]), kc) and np.array_equal(host(d["v"]), vc)
-    seqs = sample_seqs(w, 24)
-    assert_close(as_f64(out)[seqs], oracle_decode(w, kc, vc, seqs=seqs), "bf16", "fused llama70b")
-    with pytest.raises(NotImplementedError):
-        pa.decode_append(d["q"], d["k"], d["v"], dev(k), dev(v), dev(slots), d["bt"], d["lens"],
-                         w.scale, max_seq_len=w.max_seq_len, kernel="stream")
+    assert_close(as_f64(out), oracle_decode(w, kc, vc), "bf16", "fused llama70b")
 
 
 @pytest.mark.parametrize("batch", [600, 4500])
@@ -439,14 +416,12 @@ def test_longest_first_ranking_large_batches(pa, batch):
     d = upload(w)
     out = decode(pa, d, w, kernel="mfma")
     got = as_f64(out)
-    seqs = sample_seqs(w, 64, seed=batch) + [0, batch - 1]
-    seqs = sorted(set(seqs))
-    assert_close(got[seqs], oracle_decode(w, seqs=seqs), "bf16", f"B={batch}")
+    live = [s for s in range(batch) if lens[s] > 0]
+    assert_close(got[live], oracle_decode(w, seqs=live), "bf16", f"B={batch}")
     empty = [s for s in range(batch) if lens[s] == 0]
     assert np.all(got[empty] == 0.0)
     # all outputs are distinct rows (no two sequences mapped to one work item)
     rows = got[:, 0, :4]
-    live = [s for s in range(batch) if lens[s] > 0]
     assert len({tuple(r) for r in rows[live]}) == len(live)
 
 
@@ -456,7 +431,7 @@ def test_decode_with_caller_order(pa):
     (that sequence's output is unspecified, every other one is right)."""
     w = W.llama70b(num_seqs=64, append=False)
     d = upload(w)
-    seqs = sample_seqs(w, 16)
+    seqs = list(range(64))
     ref = oracle_decode(w, seqs=seqs)
     for order in (pa.longest_first(d["lens"]), torch.randperm(64, dtype=torch.int32).to(DEV)):
         out = pa.decode_ordered(d["q"], d["k"], d["v"], d["bt"], d["lens"], order, w.scale,

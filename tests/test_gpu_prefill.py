@@ -3,8 +3,8 @@
 Bar: |gpu - ref| <= 1e-2 + 2e-2 |ref| elementwise (bf16 inputs, fp32
 accumulation) against the float64 oracle on the same bf16 inputs.  Small
 ragged cases compare every row; the full-size workloads run in the launch
-configuration the benchmark times and compare a seeded sample of query rows
-(all heads, all head-dim elements) that the oracle computes one by one.
+configuration the benchmark times and compare every query row (all heads,
+all head-dim elements) with the oracle.
 """
 
 import numpy as np
@@ -99,16 +99,14 @@ def test_prefill_one_query_chunks_equal_decode(pa):
 
 
 @pytest.mark.parametrize("name", ["prefill_llama70b", "prefill_chunked"])
-def test_prefill_full_size_sampled(pa, name):
+def test_prefill_full_size_every_row(pa, name):
+    """The benchmark's launch on the full batch; every query row (all heads,
+    all head dims) against the oracle, which worker processes compute."""
+    import oracle_pool
     w = W.PREFILL_WORKLOADS[name]()
     out = host_f64(run(pa, w))
-    rng = np.random.default_rng(7)
-    rows = set(rng.choice(w.num_queries, size=40, replace=False).tolist())
-    for s in rng.choice(w.num_seqs, size=4, replace=False):
-        r = rows_of(w, int(s))
-        rows.update([r[0], r[-1]])          # a chunk's first and last query
-    rows = sorted(rows)
-    assert_close(out[rows], oracle_rows(w, rows), name)
+    ref = oracle_pool.prefill_reference(name, w.num_queries)
+    assert_close(out, ref, name)
 
 
 def test_prefill_unservable_chunks_are_nan(pa):

@@ -19,7 +19,8 @@
  * block-manager argument are host memory, and pa_swap_blocks moves blocks to
  * and from pinned host memory.  The library allocates nothing and frees
  * nothing.  Its only state is a cached compute-unit count per device (used
- * to size the shared-prefix split); every call is otherwise independent.
+ * to size the shared-prefix split) and, for pa_decode_noalloc only, one
+ * static scratch array per device; every call is otherwise independent.
  *
  * One layer's cache.  `k_cache` and `v_cache` are each
  *     [num_blocks][kv_heads][block_size][head_dim]
@@ -41,7 +42,9 @@
  *   PA_ERR_UNSUPPORTED  a shape with no kernel instance (see each call);
  *   PA_ERR_HIP          the HIP runtime reported a launch error;
  *   PA_ERR_NO_SPACE     (block manager) the pool cannot cover the request:
- *                       wait, or preempt a sequence; nothing changed.
+ *                       wait, or preempt a sequence; nothing changed;
+ *   PA_ERR_SCRATCH      (pa_decode_noalloc) the call needs more workspace
+ *                       than the library's static scratch holds.
  * On an error nothing has been launched (PA_ERR_HIP: possibly part of it).
  * Device-resident contents (table entries, slots, lengths) are read by the
  * kernels, which never access memory outside the arrays described here:
@@ -62,7 +65,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1,
   PA_ERR_UNSUPPORTED = 2,
   PA_ERR_HIP = 3,
-  PA_ERR_NO_SPACE = 4
+  PA_ERR_NO_SPACE = 4,
+  PA_ERR_SCRATCH = 5
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -221,6 +225,32 @@ pa_status pa_decode_ordered(void* out, const void* q, const void* k_cache, const
                             int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                             int32_t partition_size, void* workspace, size_t workspace_bytes,
                             int32_t dtype, int32_t kernel, void* stream);
+
+/*
+ * pa_decode_ex for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as pa_decode_ex, without the workspace: the
+ * split kernels' partials go to a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on every device it
+ * runs on until the process ends.  A call whose workspace need
+ * (pa_decode_plan's workspace_bytes) exceeds it returns PA_ERR_SCRATCH before
+ * anything is launched; 16 MiB covers, e.g., 16 sequences x 64 query heads x
+ * 16 partitions at head_dim 128 (8.5 MB).  The call allocates and frees
+ * nothing.  The scratch needs no clearing (every partial the merge reads is
+ * written by the same call first), and every call on a device shares that
+ * device's array: two pa_decode_noalloc calls that can overlap on one device
+ * (different streams, no ordering between them) race and give undefined
+ * outputs.  The first call on a device looks the array's address up once
+ * (hipGetSymbolAddress); a failed lookup returns PA_ERR_HIP.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                            int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, float scale,
+                            int32_t partition_size, int32_t dtype, int32_t kernel,
+                            void* stream);
 
 /*
  * Fused decode step: the KV append of one new token per sequence and the

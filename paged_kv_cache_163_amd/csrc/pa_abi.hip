@@ -46,6 +46,34 @@ int32_t device_cus() {
   return cus;
 }
 
+// Device scratch of pa_decode_noalloc: the split kernels' partials live here
+// instead of in a caller workspace.  One copy per device, alive until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device array: kernels and copies get the address hipGetSymbolAddress
+// returns for the current device (scratch_ptr).
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current; nullptr when the lookup fails.
+void* scratch_ptr() {
+  static std::atomic<void*> ptrs[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* v = ptrs[dev].load(std::memory_order_acquire);
+  if (v != nullptr) return v;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  ptrs[dev].store(addr, std::memory_order_release);
+  return addr;
+}
+
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 int32_t log2i(int64_t v) {
@@ -359,6 +387,7 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PA_ERR_HIP: return "HIP launch error";
     case PA_ERR_NO_SPACE: return "not enough free blocks";
+    case PA_ERR_SCRATCH: return "workspace need exceeds the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -472,6 +501,29 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                       max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
                       num_blocks, scale, partition_size, workspace, workspace_bytes, dtype,
                       PA_KERNEL_AUTO, stream);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t max_seq_len, int32_t num_seqs,
+                            int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, float scale,
+                            int32_t partition_size, int32_t dtype, int32_t kernel,
+                            void* stream) {
+  Plan plan;
+  const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
+                                 max_seq_len, partition_size, dtype, kernel, &plan);
+  if (st != PA_OK) return st;
+  if (plan.workspace > kScratchBytes) return PA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (plan.workspace > 0 && num_seqs > 0) {
+    ws = scratch_ptr();
+    if (ws == nullptr) return PA_ERR_HIP;
+  }
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                     max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
+                     num_blocks, scale, partition_size, ws, ws != nullptr ? kScratchBytes : 0,
+                     dtype, kernel, stream, nullptr, nullptr, nullptr);
 }
 
 pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,

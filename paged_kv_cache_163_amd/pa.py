@@ -38,6 +38,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_NO_SPACE = 0, 1, 2, 3, 4
+PA_ERR_SCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 PA_F32, PA_BF16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
@@ -100,6 +102,8 @@ _swap_blocks_layered = _sig("pa_swap_blocks_layered", _i32, _vp, _i64, _vp, _i64
                             _i32, _i32, _i32, _i32, _vp)
 _swap_blocks = _sig("pa_swap_blocks", _i32, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i32, _i32,
                     _i32, _i32, _vp)
+_decode_noalloc = _sig("pa_decode_noalloc", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                       _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32, _vp)
 _prefill = _sig("pa_prefill", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                 _i32, _i32, _i32, _i32, _f32, _i32, _vp)
 
@@ -111,7 +115,7 @@ EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_appe
             "pa_bm_decode_inputs", "pa_bm_sequence", "pa_bm_stats", "pa_bm_refcount",
             "pa_kv_append_layered", "pa_decode_layered", "pa_copy_blocks_layered",
             "pa_swap_blocks_layered", "pa_decode_ordered", "pa_decode_shared_prefix",
-            "pa_decode_shared_prefix_workspace_bytes"]
+            "pa_decode_shared_prefix_workspace_bytes", "pa_decode_noalloc"]
 MAX_PREFIX_GROUPS = 32
 
 
@@ -129,11 +133,18 @@ def _check(status: int, what: str) -> None:
         raise NotImplementedError(msg)
     if status == PA_ERR_NO_SPACE:
         raise NoSpace(msg)
+    if status == PA_ERR_SCRATCH:
+        raise ScratchTooSmall(msg)
     raise RuntimeError(msg)
 
 
 class NoSpace(MemoryError):
     """The block pool cannot cover the request (PA_ERR_NO_SPACE): wait or preempt."""
+
+
+class ScratchTooSmall(ValueError):
+    """pa_decode_noalloc: the call needs more workspace than the library's
+    static scratch (PA_ERR_SCRATCH); use decode() with a workspace."""
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -268,6 +279,38 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
                     _dev(v_cache, "v_cache", ndim=4), *common, float(scale), int(partition_size),
                     ws_ptr, ws_len, dt, KERNELS[kernel], _stream(stream))
     _check(st, "decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, scale, max_seq_len=None,
+                   partition_size=0, out=None, kernel="auto", stream=None):
+    """decode() through pa_decode_noalloc: no workspace; the library's static
+    device scratch holds the partials.  ScratchTooSmall when the plan needs
+    more than NOALLOC_SCRATCH_BYTES.  Calls that can overlap on one device
+    race (they share the scratch)."""
+    B, hq, d = q.shape
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k_cache and v_cache must share a dtype")
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shape does not match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must be [num_seqs]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    st = _decode_noalloc(_dev(out, "out", ndim=3), _dev(q, "q", ndim=3),
+                         _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
+                         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                         _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), B, hq, hkv, d,
+                         bs, nb, float(scale), int(partition_size), _dtype_code(q),
+                         KERNELS[kernel], _stream(stream))
+    _check(st, "decode_noalloc")
     return out
 
 

@@ -194,6 +194,29 @@ def test_host_validation_rejects_before_launch(built_lib):
     assert cp(fake, fake, None, i32(2), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID
 
 
+def test_noalloc_host_checks_before_any_device_call(built_lib):
+    """pa_decode_noalloc validates its sizes and refuses a workspace need above
+    its static scratch (PA_ERR_SCRATCH) before touching any pointer or device."""
+    lib = ctypes.CDLL(built_lib)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    fake = vp(4096)
+    fn = lib.pa_decode_noalloc
+    fn.restype = i32
+
+    def call(B=16, hq=64, hkv=8, maxlen=8192, part=32, kern=0, dt=1):
+        return fn(fake, fake, fake, fake, fake, i32(512), fake, i32(maxlen), i32(B), i32(hq),
+                  i32(hkv), i32(128), i32(16), i32(10000), ctypes.c_float(0.088), i32(part),
+                  i32(dt), i32(kern), None)
+
+    INVALID, UNSUPPORTED, SCRATCH = 1, 2, 5
+    assert call() == SCRATCH                       # 136 MB of partials > 16 MiB
+    assert call(hq=9) == INVALID
+    assert call(kern=9) == INVALID
+    assert call(dt=0, kern=2) == UNSUPPORTED
+    assert call(B=0) == 0                          # nothing to do, nothing launched
+    assert lib.pa_status_string(SCRATCH) != 0
+
+
 def test_prefill_host_validation(built_lib):
     lib = ctypes.CDLL(built_lib)
     vp = ctypes.c_void_p

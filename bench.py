@@ -74,7 +74,10 @@ def parse():
     ap.add_argument("--prefix-partition", type=int, default=0,
                     help="shared_prefix: keys per prefix partition (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle time for cpu_baseline, split over three runs")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="decode workloads: skip timing the other configs after the headline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -151,42 +154,98 @@ class HipTimer:
         self._events = []
 
 
-def blas_threads() -> int:
-    """Threads numpy's BLAS may use for the oracle's products (1 if unknown)."""
+def blas_info() -> dict:
+    """numpy's BLAS as threadpoolctl reports it: vendor, version, threads."""
     try:
         from threadpoolctl import threadpool_info
         blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        return int(max([i.get("num_threads", 1) for i in blas] or [1]))
-    except Exception:  # threadpoolctl missing: numpy BLAS thread count unknown
-        return 1
+    except Exception:  # threadpoolctl missing: nothing known
+        blas = []
+    if not blas:
+        return {"vendor": "unknown", "version": None, "threads": 1}
+    b = blas[0]
+    return {"vendor": b.get("internal_api", "unknown"), "version": b.get("version"),
+            "threads": int(b.get("num_threads", 1))}
+
+
+def host_cpus() -> int:
+    """CPUs this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _timed_runs(one_unit, seconds: float, runs: int = 3):
+    """Call one_unit() (returning units of work done) until seconds/runs pass,
+    `runs` times.  Returns [(units, wall_s, cpu_s)] per run; cpu_s is the
+    process CPU time over the run, so cpu_s / wall_s is the cores it used."""
+    out = []
+    for _ in range(runs):
+        units = 0
+        t0, c0 = time.perf_counter(), time.process_time()
+        while time.perf_counter() - t0 < seconds / runs:
+            units += one_unit()
+        out.append((units, time.perf_counter() - t0, time.process_time() - c0))
+    return out
+
+
+def _baseline_summary(runs, unit_scale: float, unit: str, sample: str) -> dict:
+    rates = sorted(u * unit_scale / w for u, w, _ in runs)
+    med = rates[len(rates) // 2]
+    cores_used = sum(c for _, _, c in runs) / sum(w for _, w, _ in runs)
+    info = blas_info()
+    return {
+        "value": round(med, 9),
+        "unit": unit,
+        "cores": max(1, int(round(cores_used))),
+        "kind": "oracle",
+        "sample": sample,
+        "runs": [round(r, 9) for r in rates],
+        "cores_used": round(cores_used, 2),
+        "blas": info,
+        "affinity_cpus": host_cpus(),
+        "logical_cpus": os.cpu_count(),
+    }
 
 
 def cpu_baseline(w, seconds: float):
-    """The oracle, as it stands, on whole-batch sequences until ~seconds pass."""
+    """The oracle, as it stands, on whole-batch sequences: three runs of
+    seconds/3 each (median reported), numpy's BLAS allowed every CPU of this
+    process's affinity mask; `cores` is the CPU time over wall time it took."""
     import numpy as np
 
     import oracle
-    threads = blas_threads()
     order = np.random.default_rng(123).permutation(w.num_seqs)
-    done, kv_bytes = 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        s = int(order[done % w.num_seqs])
+    state = {"i": 0, "seqs": 0}
+    per_tok = 2 * w.kv_heads * w.head_dim * w.elem_bytes
+
+    def one():
+        s = int(order[state["i"] % w.num_seqs])
+        state["i"] += 1
+        state["seqs"] += 1
         oracle.paged_decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.scale,
                             w.block_size, seqs=[s])
-        kv_bytes += int(w.seq_lens[s]) * 2 * w.kv_heads * w.head_dim * w.elem_bytes
-        done += 1
-    dt = time.perf_counter() - t0
-    return {
-        "value": round(kv_bytes / dt / 1e9, 6),
-        "unit": "GB/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": (f"{done} sequences of the {w.name} batch (random order, seed 123), "
-                   f"{dt:.1f} s single process, numpy float64; "
-                   f"{done / dt:.2f} seqs/s; host has {os.cpu_count()} logical CPUs"),
-        "seqs_per_s": round(done / dt, 3),
-    }
+        return int(w.seq_lens[s]) * per_tok
+
+    limits = None
+    try:
+        from threadpoolctl import threadpool_limits
+        limits = threadpool_limits(limits=host_cpus(), user_api="blas")
+    except Exception:  # threadpoolctl missing: numpy's default thread count
+        pass
+    try:
+        runs = _timed_runs(one, seconds)
+    finally:
+        if limits is not None:
+            limits.restore_original_limits()
+    total_wall = sum(wall for _, wall, _ in runs)
+    res = _baseline_summary(
+        runs, 1e-9, "GB/s",
+        f"{state['seqs']} sequences of the {w.name} batch (random order, seed 123) in 3 runs "
+        f"of {seconds / 3:.1f} s, one process, numpy float64, median run reported")
+    res["seqs_per_s"] = round(state["seqs"] / total_wall, 3)
+    return res
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, vendor figure
@@ -194,33 +253,41 @@ PREFILL_METRIC = "paged chunked prefill attention: achieved TFLOP/s (% of bf16 M
 
 
 def prefill_cpu_baseline(w, seconds: float):
-    """The oracle, as it stands, on query rows of the batch until ~seconds pass."""
+    """The oracle, as it stands, on query rows of the batch (three runs of
+    seconds/3, median reported), BLAS over this process's CPUs."""
     import numpy as np
 
     import oracle
     from paged_kv_cache_163_amd import workloads as W
     order = np.random.default_rng(123).permutation(w.num_queries)
     starts = w.query_start
-    done, flops = 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds and done < w.num_queries:
-        r = int(order[done])
+    state = {"i": 0}
+
+    def one():
+        r = int(order[state["i"] % w.num_queries])
+        state["i"] += 1
         oracle.paged_prefill(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens, w.query_lens,
                              w.scale, w.block_size, rows=[r])
         s = int(np.searchsorted(starts, r, side="right")) - 1
         pos = int(w.seq_lens[s] - w.query_lens[s] + (r - starts[s]))
-        flops += W.prefill_flops([pos + 1], [1], w.num_heads, w.head_dim)
-        done += 1
-    dt = time.perf_counter() - t0
-    return {
-        "value": round(flops / dt / 1e12, 9),
-        "unit": "TFLOP/s",
-        "cores": blas_threads(),
-        "kind": "oracle",
-        "sample": (f"{done} query rows of the {w.name} batch (random order, seed 123, each "
-                   f"with its sequence's gather), {dt:.1f} s single process, numpy float64; "
-                   f"host has {os.cpu_count()} logical CPUs"),
-    }
+        return W.prefill_flops([pos + 1], [1], w.num_heads, w.head_dim)
+
+    limits = None
+    try:
+        from threadpoolctl import threadpool_limits
+        limits = threadpool_limits(limits=host_cpus(), user_api="blas")
+    except Exception:  # threadpoolctl missing: numpy's default thread count
+        pass
+    try:
+        runs = _timed_runs(one, seconds)
+    finally:
+        if limits is not None:
+            limits.restore_original_limits()
+    return _baseline_summary(
+        runs, 1e-12, "TFLOP/s",
+        f"{state['i']} query rows of the {w.name} batch (random order, seed 123, each with its "
+        f"sequence's gather) in 3 runs of {seconds / 3:.1f} s, one process, numpy float64, "
+        "median run reported")
 
 
 def prefill_main(args, np, torch, W, pa, dev):
@@ -463,6 +530,188 @@ def layered_main(args, np, torch, W, pa, dev, layers=8):
     print(json.dumps(line), flush=True)
 
 
+class DecodeRun:
+    """One decode workload resident on the device, ready to step.
+
+    A step is the workload's copy-on-write copies, its KV append, then the
+    decode: pa_decode_ordered with the batch's longest-first order (computed
+    once: every step adds one token to every sequence, so the order holds),
+    pa_decode_shared_prefix on the shared-prefix batch, pa_decode_append with
+    `fused`, pa_decode with `rank_in_kernel`.  The K/V pools are replicated
+    `rotate` times and step i uses copy i mod rotate, so a step never finds
+    the previous step's blocks in the 256 MB MALL / L2.  `host_fill` uploads
+    the workload's seeded pools (the parity tests' bytes); otherwise the pools
+    are filled with N(0,1) on the device (timing only)."""
+
+    def __init__(self, np, torch, W, pa, dev, name, *, rotate=4, partition=0, kernel="auto",
+                 fused=False, rank_in_kernel=False, plain_decode=False, prefix_partition=0,
+                 host_fill=True):
+        self.np, self.torch, self.pa, self.W = np, torch, pa, W
+        w = self.w = W.make(name, fill=host_fill)
+        self.partition, self.kernel, self.prefix_partition = partition, kernel, prefix_partition
+
+        def to_dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        if host_fill:
+            self.pools = [(to_dev(w.k_cache), to_dev(w.v_cache)) for _ in range(max(1, rotate))]
+        else:
+            g = torch.Generator(device=dev).manual_seed(0)
+            dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+            self.pools = []
+            for _ in range(max(1, rotate)):
+                k = torch.empty(w.k_cache.shape, dtype=dt, device=dev).normal_(generator=g)
+                self.pools.append((k, torch.empty_like(k).normal_(generator=g)))
+        self.q = to_dev(w.q)
+        self.bt, self.lens = to_dev(w.block_tables), to_dev(w.seq_lens)
+        self.k_new, self.v_new = to_dev(w.k_new), to_dev(w.v_new)
+        self.slots = to_dev(w.slot_mapping)
+        self.fk, self.fv, self.fslots = (to_dev(a) for a in W.per_sequence_append(w))
+        self.fused = w.slot_mapping.shape[0] > 0 and fused
+        self.pairs = to_dev(w.cow_pairs)
+        self.out = torch.empty_like(self.q)
+        self.plan = pa.decode_plan(w.num_seqs, w.num_heads, w.kv_heads, w.head_dim,
+                                   w.block_size, w.max_seq_len, partition, self.q.dtype, kernel)
+        ws_bytes = self.plan.workspace_bytes
+        # Shared-prefix batch: every table starts with the same prefix blocks,
+        # so the shared-prefix decode attends them once for the whole group.
+        self.shared = ("prefix_blocks" in w.meta and not plain_decode and not self.fused
+                       and kernel in ("auto", "mfma"))
+        if self.shared:
+            self.groups = ([0, w.num_seqs], [int(w.meta["prefix_blocks"])])
+            ws_bytes = pa.shared_prefix_workspace_bytes(
+                w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size, w.max_seq_len,
+                w.max_blocks_per_seq, *self.groups, prefix_partition_size=prefix_partition,
+                partition_size=partition)
+        self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        self.ordered = (not rank_in_kernel and not self.fused and not self.shared
+                        and self.plan.kernel == "mfma")
+        self.order = pa.longest_first(self.lens) if self.ordered else None
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i, timer=None, ev=None):
+        w, pa = self.w, self.pa
+        kc, vc = self.pools[i % len(self.pools)]
+        if w.cow_pairs.shape[0]:
+            pa.copy_blocks(kc, vc, self.pairs)
+        if w.slot_mapping.shape[0] and not self.fused:
+            pa.kv_append(self.k_new, self.v_new, kc, vc, self.slots)
+        if ev is not None:
+            timer.record(ev[0], self.stream)
+        kw = dict(max_seq_len=w.max_seq_len, partition_size=self.partition, out=self.out,
+                  workspace=self.ws)
+        if self.fused:   # one launch: the new tokens' append and the decode
+            pa.decode_append(self.q, kc, vc, self.fk, self.fv, self.fslots, self.bt, self.lens,
+                             w.scale, kernel=self.kernel, **kw)
+        elif self.shared:
+            pa.decode_shared_prefix(self.q, kc, vc, self.bt, self.lens, w.scale, *self.groups,
+                                    prefix_partition_size=self.prefix_partition, **kw)
+        elif self.ordered:
+            pa.decode_ordered(self.q, kc, vc, self.bt, self.lens, self.order, w.scale,
+                              kernel=self.kernel, **kw)
+        else:
+            pa.decode(self.q, kc, vc, self.bt, self.lens, w.scale, kernel=self.kernel, **kw)
+        if ev is not None:
+            timer.record(ev[1], self.stream)
+
+    def timed(self, steps, warmup, first=0):
+        """(mean step ms, per-step decode ms array) over `steps` timed steps
+        after `warmup` untimed ones: HIP events around each decode call and
+        around the whole timed region, on the stream the library launches on."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(first + i)
+        torch.cuda.synchronize()
+        timer = HipTimer()
+        evs = [(timer.event(), timer.event()) for _ in range(steps)]
+        t_start, t_end = timer.event(), timer.event()
+        torch.cuda.synchronize()
+        timer.record(t_start, self.stream)
+        for i in range(steps):
+            self.step(first + warmup + i, timer, evs[i])
+        timer.record(t_end, self.stream)
+        torch.cuda.synchronize()
+        step_ms = timer.elapsed_ms(t_start, t_end) / steps
+        dec_ms = self.np.array([timer.elapsed_ms(a, b) for a, b in evs])
+        timer.close()
+        return step_ms, dec_ms
+
+    def bytes(self):
+        """(live K/V bytes the attention consumes, distinct live K/V bytes)."""
+        w, W = self.w, self.W
+        kv = W.decode_kv_bytes(w.seq_lens, w.kv_heads, w.head_dim, w.elem_bytes)
+        uniq = W.unique_kv_bytes(w.block_tables, w.seq_lens, w.block_size, w.kv_heads,
+                                 w.head_dim, w.elem_bytes)
+        return kv, uniq
+
+    def summary(self, step_ms, dec_ms):
+        np = self.np
+        kv, uniq = self.bytes()
+        dec = float(dec_ms.mean())
+        return {
+            "workload": self.w.name,
+            "call": ("pa_decode_shared_prefix" if self.shared else
+                     "pa_decode_append" if self.fused else
+                     "pa_decode_ordered" if self.ordered else "pa_decode"),
+            "partition_size": self.plan.partition_size if not self.shared else self.partition,
+            "num_partitions": self.plan.num_partitions,
+            "decode_us": {"mean": round(dec * 1e3, 2),
+                          "median": round(float(np.median(dec_ms)) * 1e3, 2),
+                          "min": round(float(dec_ms.min()) * 1e3, 2)},
+            "step_us": round(step_ms * 1e3, 2),
+            "kv_GBps": round(kv / (dec * 1e-3) / 1e9, 1),
+            "unique_kv_GBps": round(uniq / (dec * 1e-3) / 1e9, 1),
+            "frac": round(uniq / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "seqs_per_s": round(self.w.num_seqs / (step_ms * 1e-3), 1),
+        }
+
+
+# Configurations timed after the headline in the same process: (workload,
+# partition size, note).  frac = distinct live K/V bytes / decode time / 8 TB/s.
+OTHER_CONFIGS = [
+    ("shared_prefix", 0, "pa_decode_shared_prefix, library's split"),
+    ("long_context", 512, "16 partitions of 512 tokens + reduce"),
+    ("long_context", 0, "library's split"),
+    *[(W_name, 0, "append + decode") for W_name in
+      ("sweep_b16_d64", "sweep_b16_d128", "sweep_b32_d64", "sweep_b32_d128",
+       "sweep_b64_d64", "sweep_b64_d128")],
+]
+
+
+def other_configs(np, torch, W, pa, dev, steps=40, warmup=5):
+    """Decode time and HBM fraction of every other decode configuration, with
+    device-filled pools, then the paging overhead: the llama70b batch against
+    the same batch on physically consecutive blocks, in alternating rounds."""
+    res = []
+    for name, part, note in OTHER_CONFIGS:
+        run = DecodeRun(np, torch, W, pa, dev, name, partition=part, host_fill=False)
+        s = run.summary(*run.timed(steps, warmup))
+        s["note"] = note
+        res.append(s)
+        del run
+        torch.cuda.empty_cache()
+    runs = {n: DecodeRun(np, torch, W, pa, dev, n, host_fill=False)
+            for n in ("llama70b", "llama70b_contiguous")}
+    dec = {n: [] for n in runs}
+    for r in range(6):                      # alternating rounds on one box
+        for n, run in runs.items():
+            _, d = run.timed(20, 3, first=r * 100)
+            dec[n].extend(d.tolist())
+    paged = float(np.mean(dec["llama70b"]))
+    contig = float(np.mean(dec["llama70b_contiguous"]))
+    overhead = {
+        "random_placement_us": round(paged * 1e3, 2),
+        "sequential_placement_us": round(contig * 1e3, 2),
+        "overhead_pct": round(100.0 * (paged / contig - 1.0), 2),
+        "method": "pa_decode_ordered on the llama70b batch with random block placement vs "
+                  "the same batch on consecutive blocks, 6 alternating rounds of 20 steps",
+    }
+    return res, overhead
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -500,102 +749,27 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
         return
 
-    def to_dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
+    run = DecodeRun(np, torch, W, pa, dev, args.workload, rotate=args.rotate,
+                    partition=args.partition, kernel=args.kernel, fused=args.fused_append,
+                    rank_in_kernel=args.rank_in_kernel, plain_decode=args.plain_decode,
+                    prefix_partition=args.prefix_partition, host_fill=True)
+    w, plan = run.w, run.plan
+    step_ms, dec_ms = run.timed(args.steps, args.warmup)
 
-    w = W.make(args.workload)
-    pools = [(to_dev(w.k_cache), to_dev(w.v_cache)) for _ in range(max(1, args.rotate))]
-    q = to_dev(w.q)
-    bt = to_dev(w.block_tables)
-    lens = to_dev(w.seq_lens)
-    k_new, v_new, slots = to_dev(w.k_new), to_dev(w.v_new), to_dev(w.slot_mapping)
-    fk, fv, fslots = (to_dev(a) for a in W.per_sequence_append(w))
-    fused = w.slot_mapping.shape[0] > 0 and args.fused_append
-    pairs = to_dev(w.cow_pairs)
-    out = torch.empty_like(q)
-    plan = pa.decode_plan(w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size,
-                          w.max_seq_len, args.partition, q.dtype, args.kernel)
-    eff_p, nparts, ws_bytes = plan.partition_size, plan.num_partitions, plan.workspace_bytes
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-    # Every decode step adds one token to every sequence, so the batch's
-    # longest-first order holds from step to step: an engine computes it when
-    # the batch changes, not per step.
-    # Shared-prefix batch: every table starts with the same prefix blocks, so
-    # the shared-prefix decode attends them once for the whole group.
-    shared = ("prefix_blocks" in w.meta and not args.plain_decode and not fused
-              and args.kernel in ("auto", "mfma"))
-    if shared:
-        groups = ([0, w.num_seqs], [int(w.meta["prefix_blocks"])])
-        sp_bytes = pa.shared_prefix_workspace_bytes(
-            w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size, w.max_seq_len,
-            w.max_blocks_per_seq, *groups, prefix_partition_size=args.prefix_partition,
-            partition_size=args.partition)
-        ws = torch.empty(max(sp_bytes, 16), dtype=torch.uint8, device=dev)
-    ordered = not args.rank_in_kernel and not fused and not shared and plan.kernel == "mfma"
-    order = pa.longest_first(lens) if ordered else None
-
-    def step(i, ev=None):
-        kc, vc = pools[i % len(pools)]
-        if w.cow_pairs.shape[0]:
-            pa.copy_blocks(kc, vc, pairs)
-        if w.slot_mapping.shape[0] and not fused:
-            pa.kv_append(k_new, v_new, kc, vc, slots)
-        if ev is not None:
-            timer.record(ev[0], stream)
-        if fused:   # one launch: the new tokens' append and the decode
-            pa.decode_append(q, kc, vc, fk, fv, fslots, bt, lens, w.scale,
-                             max_seq_len=w.max_seq_len, partition_size=args.partition, out=out,
-                             workspace=ws, kernel=args.kernel)
-        elif shared:
-            pa.decode_shared_prefix(q, kc, vc, bt, lens, w.scale, *groups,
-                                    max_seq_len=w.max_seq_len,
-                                    prefix_partition_size=args.prefix_partition,
-                                    partition_size=args.partition, out=out, workspace=ws)
-        elif ordered:
-            pa.decode_ordered(q, kc, vc, bt, lens, order, w.scale, max_seq_len=w.max_seq_len,
-                              partition_size=args.partition, out=out, workspace=ws,
-                              kernel=args.kernel)
-        else:
-            pa.decode(q, kc, vc, bt, lens, w.scale, max_seq_len=w.max_seq_len,
-                      partition_size=args.partition, out=out, workspace=ws, kernel=args.kernel)
-        if ev is not None:
-            timer.record(ev[1], stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    timer = HipTimer()
-    evs = [(timer.event(), timer.event()) for _ in range(args.steps)]
-    t_start, t_end = timer.event(), timer.event()
-    torch.cuda.synchronize()
-    timer.record(t_start, stream)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    timer.record(t_end, stream)
-    torch.cuda.synchronize()
-    step_ms = timer.elapsed_ms(t_start, t_end) / args.steps
-    dec_ms = np.array([timer.elapsed_ms(a, b) for a, b in evs])
-    timer.close()
-
-    kv_bytes = W.decode_kv_bytes(w.seq_lens, w.kv_heads, w.head_dim, w.elem_bytes)
-    # K/V bytes of distinct live (block, slot) positions: what one pass over
-    # the pool must read when tables share blocks (equal to kv_bytes otherwise)
-    unique_bytes = W.unique_kv_bytes(w.block_tables, w.seq_lens, w.block_size, w.kv_heads,
-                                     w.head_dim, w.elem_bytes)
+    kv_bytes, unique_bytes = run.bytes()
     total_alg = (kv_bytes + 2 * w.q.nbytes + 4 * int(sum(-(-int(n) // w.block_size)
                                                         for n in w.seq_lens)) + 4 * w.num_seqs)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
+    fused, shared, ordered = run.fused, run.shared, run.ordered
+    nparts = plan.num_partitions
     kernel_name = f"decode_{plan.kernel}_kernel" + (" (fused append)" if fused else "")
     split_reduce = nparts > 1
     if shared:
         kernel_name = "shared_prefix_kernel (prefix + tails) + prefix_merge_kernel"
         split_reduce = False
     dec_avg = float(dec_ms.mean())
+    # distinct live K/V bytes over the decode call: when tables share blocks, what
+    # one pass over the pool must read (equal to kv_bytes otherwise)
     achieved = unique_bytes / (dec_avg * 1e-3) / 1e9
     # the stored counter record is for the plain decode kernel at the default plan
     plain = args.partition == 0 and args.kernel == "auto" and not fused
@@ -633,15 +807,15 @@ def main():
             "order": ("longest-first, kept across steps (pa_decode_ordered)" if ordered
                       else "index order (shared-prefix decode)" if shared
                       else "ranked inside the kernel"),
-            "shared_prefix": ({"call": "pa_decode_shared_prefix", "groups": groups[0],
-                               "prefix_blocks": groups[1],
+            "shared_prefix": ({"call": "pa_decode_shared_prefix", "groups": run.groups[0],
+                               "prefix_blocks": run.groups[1],
                                "prefix_partition": args.prefix_partition or "library's choice"}
                               if shared else None),
             "cow_pairs": int(w.cow_pairs.shape[0]),
             "kernel": plan.kernel,
-            "partition_size": eff_p,
+            "partition_size": plan.partition_size,
             "num_partitions": nparts,
-            "pool_rotation": len(pools),
+            "pool_rotation": len(run.pools),
             "parallelism": "single GPU",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -664,6 +838,12 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_other_configs and args.workload == "llama70b":
+        del run
+        torch.cuda.empty_cache()
+        others, paging = other_configs(np, torch, W, pa, dev)
+        line["other_configs"] = others
+        line["paging_overhead"] = paging
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -30,16 +30,16 @@ def block_layout(tokens: int, block_size: int) -> tuple[int, int]:
     """Blocks one unshared sequence occupies, and its unused tail slots.
 
     lihaoran.work PagedAttention explainer, section "How many tail slots
-    remain unused?": a sequence of T cached positions in blocks of b slots
-    needs the ceiling of T/b blocks; the slots left over are that many
-    blocks' capacity minus T, which lies in [0, b-1] for T > 0, and an empty
-    sequence takes no block at all.  A negative token count or a block size
-    that is not positive is an error (ValueError).
+    remain unused?": the block count is the ceiling of tokens / block_size
+    (computed here as a negated floor division of the negated count), and
+    the unused slots are the capacity of those blocks minus the tokens, a
+    number in [0, block_size - 1] for a non-empty sequence and 0 for an
+    empty one.  Negative token counts and non-positive block sizes raise
+    ValueError (the page's helper rejects them the same way).
     """
     if tokens < 0 or block_size <= 0:
         raise ValueError(f"block_layout: bad sizes tokens={tokens} block_size={block_size}")
-    whole, leftover = divmod(tokens, block_size)
-    blocks = whole if leftover == 0 else whole + 1
+    blocks = -(-tokens // block_size)
     return blocks, blocks * block_size - tokens
 
 
@@ -85,29 +85,34 @@ def to_f64(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def gather_history(k_cache, v_cache, table_row, seq_len: int, block_size: int):
-    """Logical K and V history of one sequence, one position at a time.
+    """Logical K and V history of one sequence, assembled block by block.
 
-    Follows the conceptual lookup on the zenaique.com page (code box
-    "Conceptual: PagedAttention block lookup"): every position of
-    [0, seq_len) is sent through the block table to its physical block and
-    slot, and that slot's keys and values (all KV heads) are taken in
-    position order.  Returns float64 arrays ``[seq_len, kv_heads, head_dim]``.
+    lihaoran.work explainer, section "A block table maps logical order to
+    physical storage": entry j of a sequence's table names the physical block
+    that holds logical block j, i.e. positions [j*b, (j+1)*b).  Taking the
+    first ceil(seq_len / b) entries in order, laying each named block's slots
+    end to end, and keeping the first seq_len of them rebuilds the history in
+    position order; the unused tail slots of the last block are dropped.
+    Returns float64 arrays ``[seq_len, kv_heads, head_dim]`` (all KV heads).
     """
     _, kv_heads, _, head_dim = k_cache.shape
-    keys = np.empty((seq_len, kv_heads, head_dim), dtype=np.float64)
-    values = np.empty((seq_len, kv_heads, head_dim), dtype=np.float64)
-    for position in range(seq_len):
-        block, slot = translate(table_row, position, block_size)
-        keys[position] = to_f64(k_cache[block, :, slot, :])
-        values[position] = to_f64(v_cache[block, :, slot, :])
-    return keys, values
+    blocks, _ = block_layout(seq_len, block_size)
+    if blocks == 0:
+        empty = np.empty((0, kv_heads, head_dim), dtype=np.float64)
+        return empty, empty.copy()
+    ids = [int(table_row[j]) for j in range(blocks)]
+    # a block is [kv_heads, block_size, head_dim]: put its slots first
+    keys = np.concatenate([to_f64(k_cache[p]).transpose(1, 0, 2) for p in ids], axis=0)
+    values = np.concatenate([to_f64(v_cache[p]).transpose(1, 0, 2) for p in ids], axis=0)
+    return keys[:seq_len], values[:seq_len]
 
 
 def gather_history_vectorised(k_cache, v_cache, table_row, seq_len: int, block_size: int):
-    """Same result as :func:`gather_history`, with numpy fancy indexing.
+    """Same result as :func:`gather_history`, with numpy fancy indexing of
+    every position's (block, slot) at once.
 
-    Used for the large synthetic batches; a test checks it against the
-    position-by-position loop.
+    Used for the large synthetic batches; a test checks both gathers against
+    an independent position-by-position lookup.
     """
     positions = np.arange(seq_len, dtype=np.int64)
     blocks = np.asarray(table_row, dtype=np.int64)[positions // block_size]
@@ -159,8 +164,8 @@ def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float, bloc
     """Decode attention for every sequence (or the listed ``seqs``).
 
     For each sequence: gather its history through its block table, then
-    :func:`attend`.  ``literal=True`` uses the position-by-position gather.
-    Returns float64 ``[len(seqs), num_heads, head_dim]``.
+    :func:`attend`.  ``literal=True`` uses the block-by-block gather, else the
+    fancy-index one.  Returns float64 ``[len(seqs), num_heads, head_dim]``.
     """
     q = np.asarray(q)
     if seqs is None:
@@ -205,12 +210,13 @@ def paged_decode_layered(q_layers, kv_pool, block_tables, seq_lens, scale: float
                          block_size: int, layers=None, seqs=None) -> np.ndarray:
     """Decode attention of several layers over one layered pool.
 
-    ``q_layers`` ``[num_layers, num_seqs, num_heads, head_dim]``.  Follows the
-    zenaique.com code box: for each position, the physical block and offset
-    come from the sequence's block table, and one lookup
-    ``kv_pool[block, 0 or 1, :, :, offset, :]`` fetches that position's K (or
-    V) for every layer and KV head at once; each layer then runs the same
-    scaled dot-product attention as :func:`attend`.  Returns float64
+    ``q_layers`` ``[num_layers, num_seqs, num_heads, head_dim]``.  Layout of
+    the zenaique.com code box "Conceptual: PagedAttention block lookup": a
+    physical block holds, for its block_size positions, K (index 0 of the
+    second axis) and V (index 1) of every layer and KV head.  One table per
+    sequence serves all layers: the history is rebuilt block by block as in
+    :func:`gather_history`, each named block contributing all layers at once,
+    and each layer then runs :func:`attend`.  Returns float64
     ``[len(layers), len(seqs), num_heads, head_dim]``.
     """
     q_layers = np.asarray(q_layers)
@@ -220,12 +226,14 @@ def paged_decode_layered(q_layers, kv_pool, block_tables, seq_lens, scale: float
     out = np.empty((len(layers), len(seqs), q_layers.shape[2], q_layers.shape[3]), dtype=np.float64)
     for j, s in enumerate(seqs):
         seq_len = int(seq_lens[s])
-        keys = np.empty((seq_len, num_layers) + kv_pool.shape[3:4] + kv_pool.shape[5:6])
-        values = np.empty_like(keys)
-        for position in range(seq_len):
-            block, slot = translate(block_tables[s], position, block_size)
-            keys[position] = to_f64(kv_pool[block, 0, :, :, slot, :])
-            values[position] = to_f64(kv_pool[block, 1, :, :, slot, :])
+        blocks, _ = block_layout(seq_len, block_size)
+        ids = [int(block_tables[s][i]) for i in range(blocks)]
+        # kv_pool[p, 0] is [layers, kv_heads, block_size, head_dim]: slots first
+        parts_k = [to_f64(kv_pool[p, 0]).transpose(2, 0, 1, 3) for p in ids]
+        parts_v = [to_f64(kv_pool[p, 1]).transpose(2, 0, 1, 3) for p in ids]
+        shape = (0, num_layers) + kv_pool.shape[3:4] + kv_pool.shape[5:6]
+        keys = np.concatenate(parts_k, axis=0)[:seq_len] if ids else np.empty(shape)
+        values = np.concatenate(parts_v, axis=0)[:seq_len] if ids else np.empty(shape)
         for i, layer in enumerate(layers):
             out[i, j] = attend(to_f64(q_layers[layer, s]), keys[:, layer], values[:, layer], scale)
     return out

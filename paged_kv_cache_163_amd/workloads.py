@@ -28,6 +28,15 @@ Workloads (all use ``numpy.random.default_rng(seed)``, seed 0 by default):
   in a 10,000-block pool.
 * ``sweep``: 512 sequences, lengths log-uniform in [16, 4096], 32 query /
   8 KV heads, block size in {16, 32, 64}, head_dim in {64, 128}.
+* ``llama70b_contiguous``: the llama70b batch (same lengths, queries, new
+  tokens and cache contents) with physically sequential blocks: sequence s
+  holds consecutive block ids right after sequence s - 1.  Decode over it
+  reads the same logical K/V, so its outputs equal llama70b's; timing the
+  two measures what the random placement of the table costs.
+
+Every builder takes ``fill``: with ``fill=False`` the caches are left
+unwritten (``numpy.empty``), for callers that only need the tables, lengths
+and slots and fill device pools themselves (timing runs).
 
 Configurations with a decode step (tiny, llama70b, shared_prefix, sweep)
 describe the cache *before* the step; the step writes one new token per
@@ -91,7 +100,9 @@ def _stream(seed: int, kind: int, index: int) -> np.random.Generator:
 _FILL_THREADS = max(1, min(8, os.cpu_count() or 1))
 
 
-def _nan_pool(shape, dtype: str) -> np.ndarray:
+def _nan_pool(shape, dtype: str, fill: bool = True) -> np.ndarray:
+    if not fill:
+        return np.empty(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
     if dtype == "bf16":
         return np.full(shape, BF16_NAN, dtype=np.uint16)
     return np.full(shape, np.nan, dtype=np.float32)
@@ -276,14 +287,17 @@ def _pack_tables(tables: list[list[int]], padding: int) -> np.ndarray:
 def build_private(name: str, pre_lens, *, dtype: str, num_heads: int, kv_heads: int,
                   head_dim: int, block_size: int, num_blocks: int, append: bool,
                   seed: int = 0, fixed_tables: dict | None = None, rng=None,
-                  scale: float | None = None, meta: dict | None = None) -> DecodeWorkload:
+                  scale: float | None = None, meta: dict | None = None,
+                  sequential: bool = False, fill: bool = True) -> DecodeWorkload:
     """Sequences with private blocks only.
 
     ``fixed_tables`` maps a sequence index to a block list it must use (and the
     allocator skips those ids).  Draw order on ``rng`` (default_rng(seed) unless
     the caller already drew lengths from it): placement permutation, q, new
     tokens.  Sequence s's cache contents come from its own stream
-    default_rng([seed, 7, s]).
+    default_rng([seed, 7, s]).  ``sequential`` hands blocks out in id order
+    instead of the drawn permutation (which is still drawn, so q and the new
+    tokens are the same either way).
     """
     if rng is None:
         rng = np.random.default_rng(seed)
@@ -293,6 +307,8 @@ def build_private(name: str, pre_lens, *, dtype: str, num_heads: int, kv_heads: 
     fixed_tables = fixed_tables or {}
     reserved = {b for t in fixed_tables.values() for b in t}
     order = rng.permutation(num_blocks)
+    if sequential:
+        order = np.arange(num_blocks)
     order = np.asarray([b for b in order if b not in reserved], dtype=np.int64)
     pool = BlockPool(num_blocks, order)
     padding = pool.take(1)[0]
@@ -307,9 +323,10 @@ def build_private(name: str, pre_lens, *, dtype: str, num_heads: int, kv_heads: 
             t = pool.take(need)
         tables.append(t)
     q = _draw(rng, (nseq, num_heads, head_dim), dtype)
-    k_cache = _nan_pool((num_blocks, kv_heads, bs, head_dim), dtype)
-    v_cache = _nan_pool((num_blocks, kv_heads, bs, head_dim), dtype)
-    _fill_all(seed, 7, k_cache, v_cache, tables, pre_lens, dtype)
+    k_cache = _nan_pool((num_blocks, kv_heads, bs, head_dim), dtype, fill)
+    v_cache = _nan_pool((num_blocks, kv_heads, bs, head_dim), dtype, fill)
+    if fill:
+        _fill_all(seed, 7, k_cache, v_cache, tables, pre_lens, dtype)
     if append:
         slots = np.asarray([_append_slot(tables[s], int(pre_lens[s]), bs, pool)
                             for s in range(nseq)], dtype=np.int64)
@@ -338,31 +355,40 @@ def build_private(name: str, pre_lens, *, dtype: str, num_heads: int, kv_heads: 
 # the five workloads
 # --------------------------------------------------------------------------
 
-def tiny(seed: int = 0, append: bool = True) -> DecodeWorkload:
+def tiny(seed: int = 0, append: bool = True, fill: bool = True) -> DecodeWorkload:
     """4 sequences {10, 1, 16, 37}, b=4, 8/2 heads, D=64, fp32, 32-block pool.
     Sequence 0 uses table [5, 1, 7]."""
     return build_private(
         "tiny", [10, 1, 16, 37], dtype="f32", num_heads=8, kv_heads=2, head_dim=64,
         block_size=4, num_blocks=32, append=append, seed=seed,
-        fixed_tables={0: [5, 1, 7]}, scale=1.0 / np.sqrt(64.0))
+        fixed_tables={0: [5, 1, 7]}, scale=1.0 / np.sqrt(64.0), fill=fill)
 
 
-def llama70b(seed: int = 0, num_seqs: int = 256, append: bool = True) -> DecodeWorkload:
-    """One Llama-3.1-70B-shaped layer: 256 chat sequences, bf16, b=16, 20k blocks."""
+def llama70b(seed: int = 0, num_seqs: int = 256, append: bool = True,
+             sequential: bool = False, fill: bool = True) -> DecodeWorkload:
+    """One Llama-3.1-70B-shaped layer: 256 chat sequences, bf16, b=16, 20k blocks
+    (``sequential``: the same batch on physically consecutive blocks)."""
     rng = np.random.default_rng(seed)
     prompt = rng.integers(500, 700, size=num_seqs, endpoint=True)
     generated = rng.integers(0, 250, size=num_seqs, endpoint=True)
     return build_private(
-        "llama70b", prompt + generated, dtype="bf16", num_heads=64, kv_heads=8, head_dim=128,
-        block_size=16, num_blocks=20000, append=append, rng=rng, seed=seed,
-        meta={"prompt": "U{500..700}", "generated": "U{0..250}"})
+        "llama70b_contiguous" if sequential else "llama70b", prompt + generated, dtype="bf16",
+        num_heads=64, kv_heads=8, head_dim=128, block_size=16, num_blocks=20000, append=append,
+        rng=rng, seed=seed, sequential=sequential, fill=fill,
+        meta={"prompt": "U{500..700}", "generated": "U{0..250}",
+              "placement": "sequential" if sequential else "random"})
 
 
-def long_context(seed: int = 0) -> DecodeWorkload:
+def llama70b_contiguous(seed: int = 0, fill: bool = True) -> DecodeWorkload:
+    """The llama70b batch with each sequence's blocks physically consecutive."""
+    return llama70b(seed=seed, sequential=True, fill=fill)
+
+
+def long_context(seed: int = 0, fill: bool = True) -> DecodeWorkload:
     """16 sequences x 8,192 tokens (512 blocks each) in a 10,000-block pool."""
     return build_private(
         "long_context", [8192] * 16, dtype="bf16", num_heads=64, kv_heads=8, head_dim=128,
-        block_size=16, num_blocks=10000, append=False, seed=seed)
+        block_size=16, num_blocks=10000, append=False, seed=seed, fill=fill)
 
 
 def sweep_lengths(rng: np.random.Generator, num_seqs: int) -> np.ndarray:
@@ -371,7 +397,8 @@ def sweep_lengths(rng: np.random.Generator, num_seqs: int) -> np.ndarray:
     return np.clip(np.floor(x).astype(np.int64), 16, 4096)
 
 
-def sweep(block_size: int, head_dim: int, seed: int = 0, num_seqs: int = 512) -> DecodeWorkload:
+def sweep(block_size: int, head_dim: int, seed: int = 0, num_seqs: int = 512,
+          fill: bool = True) -> DecodeWorkload:
     """512 sequences, log-uniform lengths, 32/8 heads, bf16; append then decode.
     Pool = ceil(1.25 * blocks needed after the append) + 1 padding block."""
     rng = np.random.default_rng(seed)
@@ -381,14 +408,15 @@ def sweep(block_size: int, head_dim: int, seed: int = 0, num_seqs: int = 512) ->
     return build_private(
         f"sweep_b{block_size}_d{head_dim}", lens, dtype="bf16", num_heads=32, kv_heads=8,
         head_dim=head_dim, block_size=block_size, num_blocks=num_blocks, append=True, rng=rng,
-        seed=seed, meta={"lengths": "log-uniform [16, 4096]"})
+        seed=seed, fill=fill, meta={"lengths": "log-uniform [16, 4096]"})
 
 
 SWEEP_CELLS = [(b, d) for b in (16, 32, 64) for d in (64, 128)]
 
 
 def shared_prefix(seed: int = 0, num_seqs: int = 200, num_beams: int = 16,
-                  prefix_tokens: int = 2000, num_blocks: int = 20000) -> DecodeWorkload:
+                  prefix_tokens: int = 2000, num_blocks: int = 20000,
+                  fill: bool = True) -> DecodeWorkload:
     """200 sequences on one shared 2,000-token prefix + private tails; a 16-beam
     fork with copy-on-write of the parent's partly filled last block.
 
@@ -410,10 +438,11 @@ def shared_prefix(seed: int = 0, num_seqs: int = 200, num_beams: int = 16,
             pool.share(shared)              # one more table points at the prefix
         tables.append(list(shared) + pool.take(_ceil_div(int(tails[s]), bs)))
     q = _draw(rng, (num_seqs + num_beams, num_heads, head_dim), dtype)
-    k_cache = _nan_pool((num_blocks, kv_heads, bs, head_dim), dtype)
-    v_cache = _nan_pool((num_blocks, kv_heads, bs, head_dim), dtype)
-    _fill_sequence(_stream(seed, 8, 0), k_cache, v_cache, shared, prefix_tokens, dtype)
-    _fill_all(seed, 7, k_cache, v_cache, [t[prefix_blocks:] for t in tables], tails, dtype)
+    k_cache = _nan_pool((num_blocks, kv_heads, bs, head_dim), dtype, fill)
+    v_cache = _nan_pool((num_blocks, kv_heads, bs, head_dim), dtype, fill)
+    if fill:
+        _fill_sequence(_stream(seed, 8, 0), k_cache, v_cache, shared, prefix_tokens, dtype)
+        _fill_all(seed, 7, k_cache, v_cache, [t[prefix_blocks:] for t in tables], tails, dtype)
     # fork: the first sequence whose last block is only partly filled
     parent = int(np.flatnonzero(pre_lens % bs != 0)[0])
     parent_len = int(pre_lens[parent])
@@ -594,6 +623,7 @@ WORKLOADS = {
     "llama70b": llama70b,
     "shared_prefix": shared_prefix,
     "long_context": long_context,
+    "llama70b_contiguous": llama70b_contiguous,
 }
 
 
@@ -601,11 +631,12 @@ def sweep_name(block_size: int, head_dim: int) -> str:
     return f"sweep_b{block_size}_d{head_dim}"
 
 
-def make(name: str, seed: int = 0) -> DecodeWorkload:
-    """Build a workload by name (``sweep_b{16,32,64}_d{64,128}`` for the sweep)."""
+def make(name: str, seed: int = 0, fill: bool = True) -> DecodeWorkload:
+    """Build a workload by name (``sweep_b{16,32,64}_d{64,128}`` for the sweep);
+    ``fill=False`` leaves the caches unwritten."""
     if name in WORKLOADS:
-        return WORKLOADS[name](seed=seed)
+        return WORKLOADS[name](seed=seed, fill=fill)
     if name.startswith("sweep_b"):
         b, d = name[len("sweep_b"):].split("_d")
-        return sweep(int(b), int(d), seed=seed)
+        return sweep(int(b), int(d), seed=seed, fill=fill)
     raise KeyError(f"unknown workload {name!r}")

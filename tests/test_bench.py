@@ -83,3 +83,17 @@ def test_counter_summary_sums_per_dispatch_and_takes_the_median(tmp_path):
     md = P.counters_md(str(tmp_path), "prefill_mfma_kernel", "w", "cmd")
     assert "| SQ_WAVE_CYCLES | 7.00 |" in md        # per-dispatch sums 3, 7, 11 -> median 7
     assert "median over 3 dispatches" in md
+
+
+def test_cpu_baseline_summary_takes_the_median_run_and_measured_cores():
+    """cpu_baseline: three runs, the median rate reported, `cores` = process
+    CPU time over wall time (rounded, at least 1), the runs and BLAS listed."""
+    import bench
+    runs = [(30, 2.0, 2.0), (10, 2.0, 2.1), (20, 2.0, 1.9)]       # (units, wall, cpu)
+    res = bench._baseline_summary(runs, 1.0, "u/s", "sample")
+    assert res["value"] == 10.0 and res["runs"] == [5.0, 10.0, 15.0]
+    assert res["cores"] == 1 and res["cores_used"] == 1.0
+    res = bench._baseline_summary([(8, 1.0, 3.6)], 1.0, "u/s", "sample")
+    assert res["cores"] == 4
+    assert {"vendor", "threads"} <= set(res["blas"]) and res["affinity_cpus"] >= 1
+    assert res["kind"] == "oracle"

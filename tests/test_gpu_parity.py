@@ -296,6 +296,26 @@ def test_llama70b_full(pa):
     assert_close(as_f64(o), ref, "bf16", "llama70b valu")
 
 
+def test_contiguous_placement_gives_the_same_bytes(pa):
+    """The llama70b batch on physically consecutive blocks holds the same
+    logical K/V as the randomly placed one: the decode (the benchmark's
+    ordered launch) returns the same bytes, and both match the oracle."""
+    a, b = W.llama70b(append=False), W.llama70b_contiguous()
+    b_pre = b.pre_lens
+    assert np.array_equal(a.seq_lens, b_pre) and not np.array_equal(a.block_tables,
+                                                                     b.block_tables[:, :a.block_tables.shape[1]])
+    outs = []
+    for w, lens in ((a, a.seq_lens), (b, b_pre)):
+        d = upload(w)
+        d["lens"] = dev(lens)
+        o = pa.decode_ordered(d["q"], d["k"], d["v"], d["bt"], d["lens"],
+                              pa.longest_first(d["lens"]), w.scale, max_seq_len=int(lens.max()))
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert_close(as_f64(outs[1]), oracle_decode(b, lens=b_pre), "bf16", "contiguous placement")
+
+
 def test_shared_prefix_full(pa):
     w = W.shared_prefix()
     d, out, kc, vc, _ = _full_step_and_decode(pa, w)

@@ -325,6 +325,103 @@ def pin_copy_blocks():
     return np.array_equal(k2[keep], kc[keep]) and np.array_equal(v2[keep], vc[keep])
 
 
+def _history(k_cache, v_cache, table_row, n, bs):
+    """Position-by-position lookup written here, independent of the oracle:
+    position t is slot t mod bs of the block the table names for t div bs."""
+    if n == 0:
+        shape = (0,) + k_cache.shape[1:2] + k_cache.shape[3:]
+        return np.empty(shape, k_cache.dtype), np.empty(shape, v_cache.dtype)
+    keys = np.stack([k_cache[int(table_row[t // bs]), :, t % bs, :] for t in range(n)])
+    values = np.stack([v_cache[int(table_row[t // bs]), :, t % bs, :] for t in range(n)])
+    return keys, values
+
+
+def pin_append_then_gather():
+    """Four sequences, blocks of 4, tables written out here; each appends one
+    token through its slot: A (3 tokens in block 5) fills slot 3; B (4 tokens,
+    block 2 full) opens fresh block 0, so its slot number is 0; C (6 tokens in
+    blocks 7, 1) writes block 1 slot 2; D (empty) opens fresh block 4.  After
+    the append, the test's own lookup and both oracle gathers return history +
+    new token, the decode equals contiguous attention over that, and no other
+    byte of the pool changed."""
+    rng = np.random.default_rng(17)
+    bs, hkv, hq, d, nb = 4, 2, 4, 8, 8
+    lens = [3, 4, 6, 0]
+    tables = np.array([[5, 6], [2, 0], [7, 1], [4, 3]])
+    kc = np.full((nb, hkv, bs, d), np.nan)
+    vc = np.full((nb, hkv, bs, d), np.nan)
+    keys, values = [], []
+    for s, n in enumerate(lens):
+        k = rng.standard_normal((n, hkv, d))
+        v = rng.standard_normal((n, hkv, d))
+        keys.append(k)
+        values.append(v)
+        for t in range(n):
+            kc[tables[s, t // bs], :, t % bs, :] = k[t]
+            vc[tables[s, t // bs], :, t % bs, :] = v[t]
+    slots = np.array([5 * bs + 3, 0 * bs + 0, 1 * bs + 2, 4 * bs + 0], dtype=np.int64)
+    k_new = rng.standard_normal((4, hkv, d))
+    v_new = rng.standard_normal((4, hkv, d))
+    kc0, vc0 = kc.copy(), vc.copy()
+    oracle.kv_append(kc, vc, k_new, v_new, slots, bs)
+    written = np.zeros((nb, bs), dtype=bool)
+    for s in range(4):
+        n = lens[s] + 1
+        want_k = np.concatenate([keys[s], k_new[s:s + 1]])
+        want_v = np.concatenate([values[s], v_new[s:s + 1]])
+        hk, hv = _history(kc, vc, tables[s], n, bs)
+        if not (np.array_equal(hk, want_k) and np.array_equal(hv, want_v)):
+            return False
+        for gather in (oracle.gather_history, oracle.gather_history_vectorised):
+            gk, gv = gather(kc, vc, tables[s], n, bs)
+            if not (np.array_equal(gk, want_k) and np.array_equal(gv, want_v)):
+                return False
+        written[tables[s, lens[s] // bs], lens[s] % bs] = True
+    rest_k = kc.transpose(0, 2, 1, 3)[~written].view(np.uint64)
+    rest_v = vc.transpose(0, 2, 1, 3)[~written].view(np.uint64)
+    if not (np.array_equal(rest_k, kc0.transpose(0, 2, 1, 3)[~written].view(np.uint64))
+            and np.array_equal(rest_v, vc0.transpose(0, 2, 1, 3)[~written].view(np.uint64))):
+        return False
+    q = rng.standard_normal((4, hq, d))
+    got = oracle.paged_decode(q, kc, vc, tables, np.array(lens) + 1, 0.3, bs)
+    ext_k = [np.concatenate([keys[s], k_new[s:s + 1]]) for s in range(4)]
+    ext_v = [np.concatenate([values[s], v_new[s:s + 1]]) for s in range(4)]
+    return np.array_equal(got, oracle.contiguous_decode(q, ext_k, ext_v, 0.3))
+
+
+def pin_fork_copy_on_write():
+    """A parent of 6 tokens in blocks of 4 forks two children ([P1] feature
+    table; [P2] beam-search follow-up).  They share the full first block and
+    each copies the half-filled last block before writing its own token.
+    After copy_blocks + kv_append: each child's history through its table is
+    the parent's 6 tokens + its own token, the parent's history is unchanged,
+    and the shared block is still the parent's."""
+    rng = np.random.default_rng(23)
+    bs, hkv, hq, d = 4, 2, 4, 8
+    q, kc, vc, tables, keys, values = _random_paged_batch(rng, [6], hq, hkv, d, bs, spare=3,
+                                                          poison=True)
+    p0, p1 = int(tables[0, 0]), int(tables[0, 1])
+    spare = [b for b in range(kc.shape[0]) if b not in (p0, p1)]
+    children = spare[:2]
+    kc0, vc0 = kc.copy(), vc.copy()
+    oracle.copy_blocks(kc, vc, [(p1, c) for c in children])
+    k_new = rng.standard_normal((2, hkv, d))
+    v_new = rng.standard_normal((2, hkv, d))
+    oracle.kv_append(kc, vc, k_new, v_new, np.array([c * bs + 2 for c in children]), bs)
+    for i, c in enumerate(children):
+        hk, hv = _history(kc, vc, [p0, c], 7, bs)
+        if not (np.array_equal(hk, np.concatenate([keys[0], k_new[i:i + 1]]))
+                and np.array_equal(hv, np.concatenate([values[0], v_new[i:i + 1]]))):
+            return False
+    hk, hv = _history(kc, vc, [p0, p1], 6, bs)
+    if not (np.array_equal(hk, keys[0]) and np.array_equal(hv, values[0])):
+        return False
+    untouched = [b for b in range(kc.shape[0]) if b not in children]
+    # NaN poison in the parent's tail slots: compare bit patterns
+    return (np.array_equal(kc[untouched].view(np.uint64), kc0[untouched].view(np.uint64))
+            and np.array_equal(vc[untouched].view(np.uint64), vc0[untouched].view(np.uint64)))
+
+
 def pin_bf16_decode():
     cases = {0x3F80: 1.0, 0xC000: -2.0, 0x0000: 0.0, 0x3E80: 0.25, 0x4049: 3.140625,
              0x0001: 2.0 ** -133, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127}
@@ -490,7 +587,7 @@ ALL_PINS = [
     pin_shared_prefix_equals_private, pin_append_roundtrip, pin_copy_blocks, pin_bf16_decode,
     pin_prefill_single_query_is_decode, pin_prefill_torch_sdpa_causal,
     pin_prefill_chunk_rows_of_full, pin_prefill_future_keys_ignored, pin_swap_round_trip,
-    pin_layered_equals_per_layer,
+    pin_layered_equals_per_layer, pin_append_then_gather, pin_fork_copy_on_write,
 ]
 
 
@@ -505,13 +602,22 @@ def test_block_layout_rejects_bad_sizes():
             oracle.block_layout(tokens, bs)
 
 
-def test_literal_and_vectorised_gather_agree():
+def test_both_gathers_equal_an_independent_lookup():
+    """The block-by-block gather and the fancy-index gather both equal a
+    position-by-position lookup written in this test (tiny workload, every
+    length 0..max through seq 0's table [5, 1, 7], and the empty history)."""
     w = W.tiny()
-    for s in range(w.num_seqs):
-        a = oracle.gather_history(w.k_cache, w.v_cache, w.block_tables[s], int(w.pre_lens[s]), 4)
-        b = oracle.gather_history_vectorised(w.k_cache, w.v_cache, w.block_tables[s],
-                                             int(w.pre_lens[s]), 4)
-        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    cases = [(s, int(w.pre_lens[s])) for s in range(w.num_seqs)]
+    cases += [(0, n) for n in range(0, 13)]
+    for s, n in cases:
+        hk, hv = _history(w.k_cache, w.v_cache, w.block_tables[s], n, 4)
+        for gather in (oracle.gather_history, oracle.gather_history_vectorised):
+            k, v = gather(w.k_cache, w.v_cache, w.block_tables[s], n, 4)
+            assert k.shape == (n, 2, 64) and v.shape == (n, 2, 64)
+            if n:
+                # positions past a sequence's length hold NaN poison: compare it too
+                assert np.array_equal(k, oracle.to_f64(hk), equal_nan=True)
+                assert np.array_equal(v, oracle.to_f64(hv), equal_nan=True)
 
 
 def test_capacity_arithmetic_matches_pages():
@@ -614,6 +720,52 @@ def _visible_all(position, seq_len):
     return seq_len
 
 
+def _append_kv_swapped(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
+    opa.__dict__["_orig_append"](k_cache, v_cache, v_new, k_new, slot_mapping, block_size)
+
+
+def _append_block_offset_swapped(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
+    for token, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        offset, block = divmod(int(slot), block_size)
+        if block < k_cache.shape[0] and offset < k_cache.shape[2]:
+            k_cache[block, :, offset, :] = k_new[token]
+            v_cache[block, :, offset, :] = v_new[token]
+
+
+def _append_skips_slot_zero(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    opa.__dict__["_orig_append"](k_cache, v_cache, k_new, v_new, np.where(slots == 0, -1, slots),
+                                 block_size)
+
+
+def _append_first_head_only(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
+    for token, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        block, offset = divmod(int(slot), block_size)
+        k_cache[block, 0, offset, :] = k_new[token][0]
+        v_cache[block, 0, offset, :] = v_new[token][0]
+
+
+def _copy_keys_only(k_cache, v_cache, pairs):
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        k_cache[dst] = k_cache[src]
+
+
+def _copy_reversed(k_cache, v_cache, pairs):
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        k_cache[src] = k_cache[dst]
+        v_cache[src] = v_cache[dst]
+
+
+def _copy_first_slot_only(k_cache, v_cache, pairs):
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        k_cache[dst, :, 0] = k_cache[src, :, 0]
+        v_cache[dst, :, 0] = v_cache[src, :, 0]
+
+
 def _swap_reversed(dst_k, dst_v, src_k, src_v, pairs):
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
         dst_k[src] = src_k[dst]
@@ -648,6 +800,9 @@ PLANTED = {
     "chunk_positions": [_positions_from_zero],
     "visible_prefix": [_visible_exclusive, _visible_all],
     "swap_blocks": [_swap_reversed, _swap_keys_only],
+    "kv_append": [_append_kv_swapped, _append_block_offset_swapped, _append_skips_slot_zero,
+                  _append_first_head_only],
+    "copy_blocks": [_copy_keys_only, _copy_reversed, _copy_first_slot_only],
     "layer_views": [_layer_views_kv_swapped, _layer_views_wrong_axis],
     "paged_decode_layered": [_layered_kv_swapped],
 }
@@ -668,6 +823,7 @@ def _any_pin_fails():
 def test_planted_mistake_is_caught(monkeypatch, target, bad):
     monkeypatch.setitem(opa.__dict__, "_orig_attend", opa.attend)
     monkeypatch.setitem(opa.__dict__, "_orig_layered", opa.paged_decode_layered)
+    monkeypatch.setitem(opa.__dict__, "_orig_append", opa.kv_append)
     monkeypatch.setattr(opa, target, bad)
     monkeypatch.setattr(oracle, target, bad)
     assert _any_pin_fails(), f"no pin caught the planted mistake {bad.__name__}"

@@ -135,8 +135,54 @@ def pin_ledger_random_streams():
     return True
 
 
+def _lookup(k_pool, v_pool, table, n, bs):
+    """Position-by-position read of a sequence through its table (test side)."""
+    return (np.stack([k_pool[table[t // bs], :, t % bs] for t in range(n)]),
+            np.stack([v_pool[table[t // bs], :, t % bs] for t in range(n)]))
+
+
+def pin_swap_round_trip_content():
+    """Preemption moves a sequence's content, not just its ids ("How
+    PagedAttention works", feature table: blocks swap to host memory and
+    back).  Content is moved with the oracle's block swap along the pairs the
+    manager reports; in between, another sequence reuses the freed device
+    blocks and overwrites them.  The swapped sequence read through its new
+    table afterwards is byte-identical to before, and so is the fork that
+    still shares its first block on the device."""
+    rng = np.random.default_rng(53)
+    bs, hkv, d = 4, 2, 3
+    bm = BlockManager(10, bs, num_host_blocks=6)
+    dev_k = np.full((10, hkv, bs, d), np.nan)
+    dev_v = np.full((10, hkv, bs, d), np.nan)
+    host_k = np.full((6, hkv, bs, d), np.nan)
+    host_v = np.full((6, hkv, bs, d), np.nan)
+
+    def write(seq, start, n):
+        for t in range(start, start + n):
+            blk = bm.tables[seq][t // bs]
+            dev_k[blk, :, t % bs] = rng.standard_normal((hkv, d))
+            dev_v[blk, :, t % bs] = rng.standard_normal((hkv, d))
+
+    bm.admit(1, 11)                        # 3 blocks, the last one 3/4 full
+    write(1, 0, 11)
+    bm.fork(1, 2)                          # shares all three blocks
+    slots, cow = bm.append_slots([2])      # 2 copies the shared last block
+    oracle.copy_blocks(dev_k, dev_v, cow)
+    write(2, 11, 1)
+    before1 = _lookup(dev_k, dev_v, list(bm.tables[1]), 11, bs)
+    before2 = _lookup(dev_k, dev_v, list(bm.tables[2]), 12, bs)
+    oracle.swap_blocks(host_k, host_v, dev_k, dev_v, bm.swap_out(1))
+    bm.admit(3, 8)                         # takes the device block 1 gave up
+    write(3, 0, 8)
+    oracle.swap_blocks(dev_k, dev_v, host_k, host_v, bm.swap_in(1))
+    after1 = _lookup(dev_k, dev_v, list(bm.tables[1]), 11, bs)
+    after2 = _lookup(dev_k, dev_v, list(bm.tables[2]), 12, bs)
+    same = all(np.array_equal(x, y) for x, y in zip(before1 + before2, after1 + after2))
+    return same and bm.free_host_blocks() == 6
+
+
 ALL_PINS = [pin_request_blocks, pin_admission_rule, pin_shared_prefix, pin_copy_on_write,
-            pin_ledger_random_streams]
+            pin_ledger_random_streams, pin_swap_round_trip_content]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -182,12 +228,30 @@ def _release_leaks(self, seq):
     self.swapped.discard(seq)
 
 
+def _swap_in_pairs_misordered(self, seq):
+    """Reports the (host, device) pairs in reverse while the table keeps its order."""
+    pairs = BlockManager.__dict__["_orig_swap_in"](self, seq)
+    return [(h, d) for (h, _), (_, d) in zip(pairs, reversed(pairs))]
+
+
+def _swap_out_keeps_device_ids(self, seq):
+    """Moves the blocks to the host in the ledger but leaves the table naming
+    the old device ids."""
+    table = list(self.tables[seq])
+    pairs = BlockManager.__dict__["_orig_swap_out"](self, seq)
+    self.tables[seq] = table
+    return pairs
+
+
 PLANTED = [("can_admit", _can_admit_no_growth), ("fork", _fork_no_refcount),
-           ("append_slots", _append_no_cow), ("release", _release_leaks)]
+           ("append_slots", _append_no_cow), ("release", _release_leaks),
+           ("swap_in", _swap_in_pairs_misordered), ("swap_out", _swap_out_keeps_device_ids)]
 
 
 @pytest.mark.parametrize("name,bad", PLANTED, ids=[p[0] for p in PLANTED])
 def test_planted_mistake_is_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(BlockManager, "_orig_swap_in", BlockManager.swap_in, raising=False)
+    monkeypatch.setattr(BlockManager, "_orig_swap_out", BlockManager.swap_out, raising=False)
     monkeypatch.setattr(BlockManager, name, bad)
     failed = False
     for pin in ALL_PINS:

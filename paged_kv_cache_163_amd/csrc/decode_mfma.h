@@ -2,10 +2,16 @@
 // fp32 accumulation): the work of one work-group, shared by the decode
 // kernel (decode_mfma.hip) and the shared-prefix launch (shared_prefix.hip).
 //
-// One work-group of kWaves waves per (sequence, KV head, partition), longest
+// One work-group of NW waves per (sequence, KV head, partition), longest
 // sequences first.  The partition is cut into 32-token steps (mfma_step.h);
-// wave w takes steps w, w + kWaves, ...  Loads run one step ahead of the math
-// (two register sets).
+// wave w takes steps w, w + NW, ...  Loads run one step ahead of the math
+// (two register sets).  NW = 4 by default; the plan takes 2 when a split
+// into equal partitions yields half as many work items as the GPU has wave
+// slots, so each wave walks more steps per prologue and merge.  With WP
+// ("wave per partition", for splits with at least as many items as wave
+// slots) the NW waves of a work-group take NW consecutive partitions of one
+// (sequence, KV head), each wave all the steps of its own partition, and each
+// writes its own partial: no cross-wave merge.
 // At the end the waves merge (m, l, O) through LDS; a single-partition
 // sequence writes its normalised bf16 output directly, otherwise the partial
 // goes to the workspace and decode_reduce.hip merges the partitions.
@@ -18,7 +24,7 @@ namespace {
 
 using namespace mfma;
 
-// Waves per work-group, and the minimum waves per SIMD the register
+// Default waves per work-group, and the minimum waves per SIMD the register
 // allocation must leave room for (tuning knobs; 0 = compiler's choice).
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
@@ -144,21 +150,23 @@ enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered, kModeTail };
 
 // The LDS of one decode work-group, declared by the kernel that runs it (the
 // shared-prefix launch overlays it with the prefix work-groups' staging).
-template <int D>
+template <int D, int NW = kWaves>
 struct DecodeLds {
-  float o[kWaves][16][D];  // per-wave (m, l, O) for the cross-wave merge
-  float m[kWaves][16];
-  float l[kWaves][16];
+  float o[NW][16][D];      // per-wave (m, l, O) for the cross-wave merge
+  float m[NW][16];
+  float l[NW][16];
   int hist[256];           // longest-first ranking
   int pick[2];
   __attribute__((aligned(16))) unsigned char nw[2 * D * 2];  // fused append: the new K and V rows
 };
 
-// The work of decode work-group `wg` (sequence, KV head, partition) in mode M.
-template <int D, int M>
-__device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeLds<D>& lds) {
+// The work of decode work-group `wg` (sequence, KV head, partition; with WP
+// partitions NW*part .. NW*part + NW - 1) in mode M, with NW waves.
+template <int D, int M, int NW = kWaves, bool WP = false>
+__device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeLds<D, NW>& lds) {
   constexpr int kKi = D / 32;
   constexpr bool kFused = M == kModeFused;
+  static_assert(!(WP && (kFused || M == kModeTail)), "wave-per-partition: plain modes only");
   auto& sm_o = lds.o;
   auto& sm_m = lds.m;
   auto& sm_l = lds.l;
@@ -208,7 +216,7 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
   if (!seq_len_ok(p, len) || len == 0) {
     if (w.part == 0) {
       const uint16_t fill = len == 0 ? (uint16_t)0 : (uint16_t)0x7FC0;
-      for (int i = tid; i < G * D; i += kWaves * 64) out[out_row0 * D + i] = fill;
+      for (int i = tid; i < G * D; i += NW * 64) out[out_row0 * D + i] = fill;
       if (kFused) store_new_token(p, w.seq, w.head, D * 2, tid);
     }
     return;
@@ -216,9 +224,12 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
   // Shared-prefix decode: positions before `pfx` belong to the prefix kernel.
   int pfx = 0;
   if constexpr (M == kModeTail) pfx = shared_prefix_tokens(p.prefix, w.seq);
-  // w.part * partition_size < max_seq_len by the plan; the sum with the
-  // prefix is formed in 64 bits
-  const int64_t pstart64 = (int64_t)pfx + (int64_t)w.part * p.partition_size;
+  // this wave's (WP) or this work-group's partition
+  const int part = WP ? w.part * NW + wave : w.part;
+  // part * partition_size < max_seq_len by the plan; the sum with the prefix
+  // is formed in 64 bits.  A WP wave past the last partition has no work (no
+  // barrier follows in that mode).
+  const int64_t pstart64 = (int64_t)pfx + (int64_t)part * p.partition_size;
   if (pstart64 >= len) return;
   const int pstart = (int)pstart64;
   const int pend = range_end(pstart, p.partition_size, len);
@@ -270,8 +281,8 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
   // run to pend; the math masks from pend_loop, which in fused mode stops one
   // token short in the owning partition (so no load waits for the new-token
   // slot, and a wave may meet a step that is wholly masked).
-  const int stride = 32 * kWaves;
-  int base = pstart + 32 * wave;
+  const int stride = WP ? 32 : 32 * NW;
+  int base = WP ? pstart : pstart + 32 * wave;
   if (base < pend) {
     StepRegs<D> ra, rb;
     load_step<D>(ra, c, base, r16, q4, bad);
@@ -294,13 +305,39 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
     add_token<D>(a, qb, sm_new, sm_new + D * 2, p.scale_log2, r16, q4);
   }
   finish_wave(a, bad);
-  stash_wave<D, kWaves>(a, sm_o, sm_m, sm_l, wave, r16, q4, G);
+  stash_wave<D, NW>(a, sm_o, sm_m, sm_l, wave, r16, q4, G);
+  if constexpr (WP) {
+    // each wave stores its own partition's result from its own stash (one
+    // wave's LDS operations complete in order)
+    // in 16-byte parts: four consecutive head dims per lane and store
+    __builtin_amdgcn_wave_barrier();
+    for (int i = 4 * lane; i < G * D; i += 4 * 64) {
+      const int g = i / D;
+      const int d = i - g * D;
+      const f32x4 o = *(const f32x4*)&sm_o[wave][g][d];
+      const float l = sm_l[wave][g];
+      if (nparts == 1) {
+        const float inv = 1.0f / l;
+        *(u32x2*)(out + (out_row0 + g) * D + d) =
+            u32x2{(uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16),
+                  (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16)};
+      } else {
+        const int64_t slot = (out_row0 + g) * p.num_partitions + part;
+        *(f32x4*)(ws_o + slot * D + d) = o;
+        if (d == 0) {
+          ws_ml[slot * 2 + 0] = sm_m[wave][g];
+          ws_ml[slot * 2 + 1] = l;
+        }
+      }
+    }
+    return;
+  }
   __syncthreads();
-  for (int i = tid; i < G * D; i += kWaves * 64) {
+  for (int i = tid; i < G * D; i += NW * 64) {
     const int g = i / D;
     const int d = i - g * D;
     float mx, l, o;
-    merge_waves<D, kWaves>(sm_o, sm_m, sm_l, g, d, mx, l, o);
+    merge_waves<D, NW>(sm_o, sm_m, sm_l, g, d, mx, l, o);
     if (nparts == 1 && pfx == 0) {
       out[(out_row0 + g) * D + d] = f32_to_bf16(o / l);
     } else {

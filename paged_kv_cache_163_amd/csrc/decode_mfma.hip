@@ -5,42 +5,66 @@
 namespace pa {
 namespace {
 
-template <int D, int M>
-__global__ __launch_bounds__(kWaves * 64)
+template <int D, int M, int NW, bool WP>
+__global__ __launch_bounds__(NW * 64)
 #if PA_MFMA_MIN_WAVES_PER_EU > 0
 __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES_PER_EU)))
 #endif
 void decode_mfma_kernel(DecodeParams p) {
-  __shared__ DecodeLds<D> lds;
-  decode_wg<D, M>(p, blockIdx.x, lds);
+  __shared__ DecodeLds<D, NW> lds;
+  decode_wg<D, M, NW, WP>(p, blockIdx.x, lds);
+}
+
+template <int D, int NW, bool WP>
+hipError_t launch_nw(const DecodeParams& p, int mode, dim3 grid, hipStream_t stream) {
+  const dim3 block(NW * 64);
+  if (mode == kModeLayered)
+    decode_mfma_kernel<D, kModeLayered, NW, WP><<<grid, block, 0, stream>>>(p);
+  else if (mode == kModeOrdered)
+    decode_mfma_kernel<D, kModeOrdered, NW, WP><<<grid, block, 0, stream>>>(p);
+  else
+    decode_mfma_kernel<D, kModePlain, NW, WP><<<grid, block, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, int mode, dim3 grid, hipStream_t stream) {
+  if (mode == kModeFused) {  // the fused append keeps one partition per work-group
+    const dim3 block(p.waves * 64);
+    if (p.waves == 4 && !p.wave_parts)
+      decode_mfma_kernel<D, kModeFused, 4, false><<<grid, block, 0, stream>>>(p);
+    else if (p.waves == 2 && !p.wave_parts)
+      decode_mfma_kernel<D, kModeFused, 2, false><<<grid, block, 0, stream>>>(p);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  if (p.wave_parts) {
+    if (p.waves != 4) return hipErrorInvalidValue;
+    return launch_nw<D, 4, true>(p, mode, grid, stream);
+  }
+  switch (p.waves) {
+    case 2: return launch_nw<D, 2, false>(p, mode, grid, stream);
+    case 4: return launch_nw<D, 4, false>(p, mode, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.num_partitions * p.num_seqs * p.kv_heads),
+  // with wave-per-partition work-groups, one work-group covers `waves` partitions
+  const int64_t groups = p.wave_parts ? (p.num_partitions + p.waves - 1) / p.waves
+                                      : p.num_partitions;
+  const dim3 grid((unsigned)(groups * p.num_seqs * p.kv_heads),
                   (unsigned)(p.num_layers > 1 ? p.num_layers : 1));
-  const dim3 block(kWaves * 64);
   const int mode = p.block_stride != 0     ? kModeLayered
                    : p.new_slots != nullptr ? kModeFused
                    : p.order != nullptr     ? kModeOrdered
                                             : kModePlain;
-#define PA_LAUNCH(DIM, MODE) decode_mfma_kernel<DIM, MODE><<<grid, block, 0, stream>>>(p)
-  if (head_dim == 128) {
-    if (mode == kModeLayered) PA_LAUNCH(128, kModeLayered);
-    else if (mode == kModeFused) PA_LAUNCH(128, kModeFused);
-    else if (mode == kModeOrdered) PA_LAUNCH(128, kModeOrdered);
-    else PA_LAUNCH(128, kModePlain);
-  } else if (head_dim == 64) {
-    if (mode == kModeLayered) PA_LAUNCH(64, kModeLayered);
-    else if (mode == kModeFused) PA_LAUNCH(64, kModeFused);
-    else if (mode == kModeOrdered) PA_LAUNCH(64, kModeOrdered);
-    else PA_LAUNCH(64, kModePlain);
-  } else {
-    return hipErrorInvalidValue;
-  }
-#undef PA_LAUNCH
-  return hipGetLastError();
+  if (head_dim == 128) return launch_d<128>(p, mode, grid, stream);
+  if (head_dim == 64) return launch_d<64>(p, mode, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

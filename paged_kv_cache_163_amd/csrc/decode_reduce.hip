@@ -6,9 +6,13 @@
 //     out = (sum_p w_p o_p) / (sum_p w_p l_p),
 // the same softmax-weighted average as one pass over the whole history.
 //
-// One 128-thread work-group per (sequence, query head): the weights w_p are
-// computed once into LDS, then each thread sums one head-dim element over the
-// partitions (consecutive threads read consecutive elements of o_p).
+// One 128-thread work-group per (sequence, query head); thread d owns output
+// element d.  Up to kRegParts partitions, every thread loads all partitions'
+// (m_p, l_p) (the same addresses for the whole work-group, so scalar loads)
+// and its own o_p[d] in one round of loads and merges in registers: one
+// memory latency and no barrier.  Longer lists compute the weights w_p once
+// into LDS, then each thread sums its element over the partitions
+// (consecutive threads read consecutive elements of o_p).
 #include <math.h>
 
 #include "pa_internal.h"
@@ -17,6 +21,7 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 128;
+constexpr int kRegParts = 32;
 
 __device__ inline float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -49,6 +54,40 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
   const int64_t slot0 = ((int64_t)seq * p.num_heads + hq) * p.num_partitions;
   const int64_t layer = blockIdx.y;  // layered pool: one grid row per decoded layer
   const float* ml = p.ws_ml + layer * (p.layer_ws_stride / D) * 2 + slot0 * 2;
+  const float* o = p.ws_o + layer * p.layer_ws_stride + slot0 * D;
+  const int d0 = threadIdx.x;
+  if (nparts <= kRegParts) {
+    if (d0 >= D) return;
+    float mv[kRegParts], lv[kRegParts], ov[kRegParts];
+#pragma unroll
+    for (int q = 0; q < kRegParts; ++q) {
+      if (q < nparts) {
+        mv[q] = ml[2 * q];
+        lv[q] = ml[2 * q + 1];
+        ov[q] = o[(int64_t)q * D + d0];
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kRegParts; ++q)
+      if (q < nparts) mx = fmaxf(mx, mv[q]);
+    float l = 0.f, acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < kRegParts; ++q) {
+      if (q < nparts) {
+        const float w = exp2f(mv[q] - mx);
+        l += w * lv[q];
+        acc += w * ov[q];
+      }
+    }
+    const float r = acc / l;
+    const int64_t idx = layer * p.layer_q_stride + ((int64_t)seq * p.num_heads + hq) * D + d0;
+    if (BF16)
+      ((uint16_t*)p.out)[idx] = f32_to_bf16(r);
+    else
+      ((float*)p.out)[idx] = r;
+    return;
+  }
 
   float mx = -INFINITY;
   for (int q = threadIdx.x; q < nparts; q += kThreads) mx = fmaxf(mx, ml[2 * q]);
@@ -61,7 +100,6 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeParams p)
   }
   l = block_sum(l, red);  // its barriers also publish sm_w
   const float inv = 1.0f / l;
-  const float* o = p.ws_o + layer * p.layer_ws_stride + slot0 * D;
   for (int d = threadIdx.x; d < D; d += kThreads) {
     float acc = 0.f;
     for (int q = 0; q < nparts; ++q) acc += sm_w[q] * o[(int64_t)q * D + d];

@@ -90,8 +90,39 @@ struct Plan {
   int32_t kernel;      // PA_KERNEL_VALU or PA_KERNEL_MFMA
   int32_t partition;   // tokens per partition
   int32_t partitions;  // grid extent along partitions
+  int32_t waves;       // matrix-core kernel: waves per work-group
+  int32_t wave_parts;  // matrix-core kernel: 1 = a partition per wave
   size_t workspace;    // bytes
 };
+
+// Work-group shape of the matrix-core decode.  Whole sequences (one
+// partition each) vary in length, and four-wave work-groups, each wave taking
+// every fourth 32-token step, dispatched longest first, keep the compute
+// units evenly loaded to the end of the launch.  Equal partitions of a split
+// need no such balance; what costs there is the fixed work per wave (the
+// prologue, the cross-wave merge, the partial store), so each wave should
+// walk many steps.  The GPU holds 8 waves per compute unit at this kernel's
+// register use (two per SIMD).  A split with at least that many work items
+// gives each wave of a four-wave work-group a partition of its own ("wave
+// per partition": no cross-wave merge); one with half as many takes two-wave
+// work-groups.  Measured on 16 sequences x 8,192 tokens x 8 KV heads (decode
+// + reduce, one box): 512-token partitions (2,048 items) 94.6 us with a
+// partition per wave, against 101.6-102.3 us with two or four waves sharing
+// each partition (95.6 us with single-wave work-groups); 1,024-token
+// partitions 89.8 us with two-wave work-groups against 91.0 with four;
+// 2,048-token partitions (512 items) 88.4 us with four.
+constexpr int32_t kWaveSlotsPerCu = 8;
+struct WgShape {
+  int32_t waves;
+  int32_t wave_parts;
+};
+WgShape decode_shape(int64_t parts, int64_t grid) {
+  if (parts <= 1) return {4, 0};
+  const int64_t slots = (int64_t)kWaveSlotsPerCu * device_cus();
+  if (grid >= slots) return {4, 1};
+  if (grid >= slots / 2) return {2, 0};
+  return {4, 0};
+}
 
 bool valu_supports(int32_t dtype, int32_t head_dim, int32_t group, int32_t block_size) {
   (void)dtype;
@@ -157,6 +188,9 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32
   plan->kernel = chosen;
   plan->partition = (int32_t)part;
   plan->partitions = (int32_t)parts;
+  const WgShape shape = chosen == PA_KERNEL_MFMA ? decode_shape(parts, grid) : WgShape{1, 0};
+  plan->waves = shape.waves;
+  plan->wave_parts = shape.wave_parts;
   plan->workspace = parts > 1 ? (size_t)num_seqs * num_heads * parts * (head_dim + 2) * 4 : 0;
   return PA_OK;
 }
@@ -361,6 +395,9 @@ static pa_status decode_impl(void* out, const void* q, const void* k_cache, cons
   p.block_shift = log2i(block_size);
   p.partition_size = plan.partition;
   p.num_partitions = plan.partitions;
+  // the fused append keeps one partition per work-group
+  p.waves = fused && plan.wave_parts ? 4 : plan.waves;
+  p.wave_parts = fused ? 0 : plan.wave_parts;
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
 
   const hipStream_t s = (hipStream_t)stream;
@@ -578,6 +615,8 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
   p.block_shift = log2i(block_size);
   p.partition_size = plan.partition;
   p.num_partitions = plan.partitions;
+  p.waves = 4;  // the tail work-groups of the shared-prefix launch
+  p.wave_parts = 0;
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   p.num_layers = 1;
   p.prefix = pg;

@@ -67,6 +67,8 @@ struct DecodeParams {
   int32_t block_shift;          // log2(block_size)
   int32_t partition_size;       // tokens per partition
   int32_t num_partitions;       // grid extent along partitions
+  int32_t waves;                // matrix-core kernel: waves per work-group (2 or 4)
+  int32_t wave_parts;           // matrix-core kernel: 1 = each wave owns one partition
   float scale_log2;             // scale * log2(e): scores kept in base-2 units
   // Layered pool (decode over [NB][2][L][Hkv][BS][D]): k_cache / v_cache point
   // at the first decoded layer's K / V, blocks lie block_stride elements

@@ -378,9 +378,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
  * table maps logical order to physical storage": full causal attention over
  * the visible history).
  *
- *   out, q         [num_queries][num_heads][head_dim] bf16; sequence s owns
+ *   out, q         [num_queries][num_heads][head_dim], dtype; sequence s owns
  *                  rows [query_start[s], query_start[s+1])
- *   k_cache,       [num_blocks][kv_heads][block_size][head_dim] bf16
+ *   k_cache,       [num_blocks][kv_heads][block_size][head_dim], dtype
  *   v_cache
  *   block_tables   int32 [num_seqs][max_blocks_per_seq]
  *   seq_lens       int32 [num_seqs]: cached positions, chunk included; the
@@ -396,10 +396,13 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
  * makes the rows that read it NaN.  Host checks: negative sizes, a zero
  * size, num_heads % kv_heads != 0, a scale that is not finite and positive
  * (the kernel takes row maxima of unscaled scores), null or misaligned
- * pointers -> PA_ERR_INVALID_ARG; fp32, head_dim not 64/128, block_size not a
- * power of two in [16, 256], or a query group (num_heads / kv_heads) that is
- * not a power of two <= 16 -> PA_ERR_UNSUPPORTED.  num_seqs, num_queries or
- * max_query_len of 0 launch nothing.
+ * pointers -> PA_ERR_INVALID_ARG.  Kernels: bf16 with block_size a power of
+ * two in [16, 256] and a query group (num_heads / kv_heads) that is a power
+ * of two <= 16 runs on the matrix cores; fp32, or bf16 with a smaller power
+ * of two block size, runs on the vector ALUs with a query group in
+ * {1, 2, 4, 8}; head_dim 64 or 128 for both.  Other shapes ->
+ * PA_ERR_UNSUPPORTED.  num_seqs, num_queries or max_query_len of 0 launch
+ * nothing.
  */
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -453,10 +456,12 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const
  * pa_decode_layered      decode of layers [first_layer, first_layer + layers)
  *                        in ONE launch (grid over layers): q and out are
  *                        [layers][num_seqs][num_heads][head_dim]; every layer
- *                        uses the same tables and lengths.  bf16 on the
- *                        matrix-core kernel only (other shapes or fp32 ->
- *                        PA_ERR_UNSUPPORTED); the workspace is `layers` times
- *                        pa_decode_plan's for one layer.  layers <= 65535.
+ *                        uses the same tables and lengths.  The kernel is
+ *                        pa_decode's automatic choice (matrix cores for
+ *                        bf16 at block sizes >= 16, else the vector-ALU
+ *                        kernel, fp32 included); the workspace is `layers`
+ *                        times pa_decode_plan's for one layer (kernel
+ *                        PA_KERNEL_AUTO).  layers <= 65535.
  * pa_copy_blocks_layered copy-on-write of whole blocks (every layer, K and V).
  * pa_swap_blocks_layered pa_swap_blocks of whole layered blocks between a
  *                        device pool and a pinned-host pool (or two device

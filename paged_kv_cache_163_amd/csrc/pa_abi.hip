@@ -334,10 +334,7 @@ static pa_status decode_impl(void* out, const void* q, const void* k_cache, cons
   const pa_status st = make_plan(num_seqs, num_heads, kv_heads, head_dim, block_size,
                                  max_seq_len, partition_size, dtype, kernel, &plan);
   if (st != PA_OK) return st;
-  if (lay != nullptr) {  // layered pools run on the matrix-core kernel only
-    if (plan.kernel != PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
-    plan.workspace *= (size_t)lay->layers;
-  }
+  if (lay != nullptr) plan.workspace *= (size_t)lay->layers;  // a partial set per layer
   if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
@@ -668,9 +665,13 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
       max_blocks_per_seq <= 0 || !dtype_ok(dtype) || !isfinite(scale) || !(scale > 0.0f))
     return PA_ERR_INVALID_ARG;
   const int32_t group = num_heads / kv_heads;
-  if (dtype != PA_BF16 || (head_dim != 64 && head_dim != 128) || !pow2(block_size) ||
-      block_size < 16 || block_size > 256 || !pow2(group) || group > 16)
-    return PA_ERR_UNSUPPORTED;
+  // the matrix-core kernel for bf16 at block sizes >= 16, the vector-ALU one
+  // for fp32 and smaller blocks
+  const bool mfma = dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) &&
+                    pow2(block_size) && block_size >= 16 && block_size <= 256 && pow2(group) &&
+                    group <= 16;
+  const bool valu = valu_supports(dtype, head_dim, group, block_size);
+  if (!mfma && !valu) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_queries == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start)
     return PA_ERR_INVALID_ARG;
@@ -680,6 +681,8 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
   const int64_t q_tiles = ceil_div((int64_t)max_query_len * group, pa::kPrefillRows);
   const int64_t pairs8 = round_up((int64_t)num_seqs * kv_heads, 8);
   if (pairs8 * q_tiles > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (!mfma && ceil_div(max_query_len, pa::kPrefillValuRows) * num_seqs * kv_heads > INT32_MAX)
+    return PA_ERR_INVALID_ARG;
 
   pa::PrefillParams p;
   memset(&p, 0, sizeof(p));
@@ -702,6 +705,8 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
   p.block_shift = log2i(block_size);
   p.q_tiles = (int32_t)q_tiles;
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  if (!mfma)
+    return from_hip(pa::launch_prefill_valu(p, dtype == PA_BF16, head_dim, (hipStream_t)stream));
   return from_hip(pa::launch_prefill_mfma(p, head_dim, (hipStream_t)stream));
 }
 
@@ -788,7 +793,7 @@ pa_status pa_decode_layered(void* out, const void* q, const void* kv_pool, int32
   const void* v = kv_pool ? base + ((int64_t)num_layers + first_layer) * layer_elems * eb : nullptr;
   return decode_impl(out, q, k, v, block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
                      num_seqs, num_heads, kv_heads, head_dim, block_size, num_blocks, scale,
-                     partition_size, workspace, workspace_bytes, dtype, PA_KERNEL_MFMA, stream,
+                     partition_size, workspace, workspace_bytes, dtype, PA_KERNEL_AUTO, stream,
                      nullptr, nullptr, nullptr, &lay);
 }
 

@@ -93,9 +93,9 @@ struct DecodeParams {
 
 // Everything a chunked-prefill launch needs.
 struct PrefillParams {
-  void* out;                    // [T][Hq][D] bf16
-  const void* q;                // [T][Hq][D] bf16: sequence s's chunk is rows query_start[s]..
-  const void* k_cache;          // [NB][Hkv][BS][D] bf16, the chunks already appended
+  void* out;                    // [T][Hq][D] dtype
+  const void* q;                // [T][Hq][D] dtype: sequence s's chunk is rows query_start[s]..
+  const void* k_cache;          // [NB][Hkv][BS][D] dtype, the chunks already appended
   const void* v_cache;
   const int32_t* block_tables;  // [B][max_blocks_per_seq]
   const int32_t* seq_lens;      // [B] cached positions, chunk included
@@ -235,8 +235,17 @@ hipError_t launch_move_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, cons
 constexpr int kPrefillRows = 128;
 hipError_t launch_prefill_mfma(const PrefillParams& p, int head_dim, hipStream_t stream);
 
+// Vector-ALU decode: fp32 or bf16, head_dim in {64, 128}, group in {1,2,4,8},
+// any power-of-two block size; per-layer or layered pools (grid y = layers).
 hipError_t launch_decode_valu(const DecodeParams& p, bool is_bf16, int head_dim,
                               hipStream_t stream);
+
+// Vector-ALU chunked prefill for the shapes the matrix-core prefill does not
+// take (fp32, block sizes below 16): same arguments and results.  A
+// work-group covers kPrefillValuRows chunk queries of one (sequence, KV head).
+constexpr int kPrefillValuRows = 8;
+hipError_t launch_prefill_valu(const PrefillParams& p, bool is_bf16, int head_dim,
+                               hipStream_t stream);
 
 // bf16 only; head_dim in {64, 128}; block_size >= 16; group <= 16;
 // partition_size a multiple of 32.

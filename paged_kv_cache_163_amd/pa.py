@@ -16,7 +16,7 @@ Tensor layouts (C-contiguous):
     block_mapping       int64 [num_pairs, 2]   (src, dst)
     kv_pool (layered)   [num_blocks, 2, num_layers, kv_heads, block_size, head_dim]
     layered q, out      [layers, num_seqs, num_heads, head_dim]
-    prefill q, out      [num_queries, num_heads, head_dim]       bfloat16
+    prefill q, out      [num_queries, num_heads, head_dim]       float32 | bfloat16
     query_start         int32 [num_seqs + 1]   chunk offsets into the prefill q
 """
 
@@ -436,7 +436,7 @@ def decode_append(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_tables,
 
 def prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start, scale, max_query_len=None,
             out=None, stream=None):
-    """Chunked causal prefill over the paged cache (bf16).
+    """Chunked causal prefill over the paged cache (bf16 or float32).
 
     Sequence s's chunk is rows query_start[s]..query_start[s+1] of ``q``; its
     queries are the last positions of the seq_lens[s] cached ones (their K/V
@@ -642,7 +642,8 @@ def decode_layered(q, kv_pool, block_tables, seq_lens, scale, first_layer=0, max
         raise ValueError("block_tables [num_seqs, max_blocks], seq_lens [num_seqs]")
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if B > 0 else 0
-    ws = decode_plan(B, hq, hkv, d, bs, max_seq_len, partition_size, q.dtype, "mfma").workspace_bytes * L
+    ws = decode_plan(B, hq, hkv, d, bs, max_seq_len, partition_size, q.dtype,
+                     "auto").workspace_bytes * L
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype:

@@ -556,7 +556,7 @@ def prefill_flops(seq_lens, query_lens, num_heads: int, head_dim: int) -> int:
 
 def build_prefill(name: str, seq_lens, query_lens, *, dtype: str, num_heads: int, kv_heads: int,
                   head_dim: int, block_size: int, num_blocks: int, seed: int = 0,
-                  meta: dict | None = None) -> PrefillWorkload:
+                  meta: dict | None = None, fixed_tables: dict | None = None) -> PrefillWorkload:
     """Private blocks holding every position (build_private with no append), and
     the chunks' queries, 256 rows per stream default_rng([seed, 13, i])."""
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
@@ -565,7 +565,7 @@ def build_prefill(name: str, seq_lens, query_lens, *, dtype: str, num_heads: int
         raise ValueError("a chunk cannot be longer than its sequence")
     base = build_private(name, seq_lens, dtype=dtype, num_heads=num_heads, kv_heads=kv_heads,
                          head_dim=head_dim, block_size=block_size, num_blocks=num_blocks,
-                         append=False, seed=seed)
+                         append=False, seed=seed, fixed_tables=fixed_tables)
     q = _draw_rows(seed, 13, (int(query_lens.sum()), num_heads, head_dim), dtype)
     return PrefillWorkload(
         name=name, dtype=dtype, num_heads=num_heads, kv_heads=kv_heads, head_dim=head_dim,
@@ -576,15 +576,26 @@ def build_prefill(name: str, seq_lens, query_lens, *, dtype: str, num_heads: int
 
 
 def prefill_tiny(seed: int = 0, head_dim: int = 64, block_size: int = 16,
-                 group: int = 4) -> PrefillWorkload:
+                 group: int = 4, dtype: str = "bf16") -> PrefillWorkload:
     """Ragged chunks: whole prompts, chunks after a cached prefix, single
-    queries, a sequence with no chunk.  bf16, 2 KV heads."""
+    queries, a sequence with no chunk.  2 KV heads."""
     seq_lens = [37, 16, 5, 300, 64, 1, 40, 129]
     query_lens = [37, 9, 5, 70, 1, 1, 0, 129]
     need = sum(_ceil_div(n, block_size) for n in seq_lens)
-    return build_prefill("prefill_tiny", seq_lens, query_lens, dtype="bf16",
+    return build_prefill("prefill_tiny", seq_lens, query_lens, dtype=dtype,
                          num_heads=2 * group, kv_heads=2, head_dim=head_dim,
                          block_size=block_size, num_blocks=need + 8, seed=seed)
+
+
+def prefill_tiny_fp32(seed: int = 0) -> PrefillWorkload:
+    """The tiny decode shape prefilled: float32, blocks of 4, 8 query / 2 KV
+    heads, head_dim 64, pool of 32 blocks, sequences of 10, 1, 16 and 37
+    positions with sequence 0 on table [5, 1, 7] (the lihaoran.work example);
+    chunks: the whole 10-token prompt, the single token, the last 7 of 16 and
+    the last 20 of 37."""
+    return build_prefill("prefill_tiny_fp32", [10, 1, 16, 37], [10, 1, 7, 20], dtype="f32",
+                         num_heads=8, kv_heads=2, head_dim=64, block_size=4, num_blocks=32,
+                         seed=seed, fixed_tables={0: [5, 1, 7]})
 
 
 def prefill_llama70b(seed: int = 0, num_seqs: int = 32) -> PrefillWorkload:

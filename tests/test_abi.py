@@ -245,13 +245,17 @@ def test_prefill_host_validation(built_lib):
     assert call(dt=5) == INVALID
     assert call(qs=None) == INVALID
     assert call(q=vp(4100)) == INVALID                # not 16-byte aligned
-    assert call(dt=0) == UNSUPPORTED                  # fp32: no prefill kernel
+    # fp32 and blocks below 16 tokens run on the vector ALUs, groups up to 8
+    assert call(dt=0, hq=32, hkv=2) == UNSUPPORTED
+    assert call(bs=8, hq=32, hkv=2) == UNSUPPORTED
     assert call(d=96) == UNSUPPORTED
-    assert call(bs=8) == UNSUPPORTED                  # block below a 16-token tile
+    assert call(bs=12) == UNSUPPORTED                 # not a power of two
     assert call(hq=6, hkv=2) == UNSUPPORTED           # group of 3
     assert call(hq=64, hkv=2) == UNSUPPORTED          # group of 32
-    # a grid beyond 2^31 work-groups
+    # a grid beyond 2^31 work-groups, either kernel
     assert call(B=1 << 20, hkv=2, maxq=1 << 20, T=1 << 20) == INVALID
+    # (vector-ALU prefill: 2^17 row tiles x 2^14 sequences x 2 KV heads = 2^32)
+    assert call(dt=0, bs=4, B=1 << 14, hkv=2, maxq=1 << 20, T=1 << 20) == INVALID
     for empty in (dict(B=0), dict(T=0), dict(maxq=0)):
         assert call(**empty) == 0                     # nothing to do, nothing launched
 

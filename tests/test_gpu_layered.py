@@ -86,6 +86,63 @@ def test_layered_decode_matches_oracle(pa, first, count, partition):
     assert_close(got, ref, f"layers {first}..{first + count - 1} P={partition}")
 
 
+def _tiny_layered(dtype, layers, seed=21):
+    """The tiny decode shape (8 query / 2 KV heads, head_dim 64, blocks of 4,
+    table [5, 1, 7] for sequence 0) over a layered pool of `layers` layers:
+    layer 0 is the seeded tiny cache, the others fresh draws with the same
+    dead (NaN) slots."""
+    base = W.build_private("tiny_layered", [10, 1, 16, 37], dtype=dtype, num_heads=8,
+                           kv_heads=2, head_dim=64, block_size=4, num_blocks=32, append=False,
+                           seed=0, fixed_tables={0: [5, 1, 7]}, scale=0.125)
+    rng = np.random.default_rng(seed)
+
+    def draw(shape):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        return W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    dead = (base.k_cache == W.BF16_NAN) if dtype == "bf16" else np.isnan(base.k_cache)
+    nan = W.BF16_NAN if dtype == "bf16" else np.float32("nan")
+    ks, vs = [base.k_cache], [base.v_cache]
+    for _ in range(layers - 1):
+        k, v = draw(base.k_cache.shape), draw(base.k_cache.shape)
+        k[dead] = nan
+        v[dead] = nan
+        ks.append(k)
+        vs.append(v)
+    pool = np.ascontiguousarray(np.stack([np.stack(ks, 1), np.stack(vs, 1)], 1))
+    q = draw((layers,) + base.q.shape)
+    return base, pool, q
+
+
+def to_dev(arr):
+    return dev(arr) if arr.dtype == np.uint16 else torch.from_numpy(arr).to(DEV)
+
+
+@pytest.mark.parametrize("first,count,partition", [(0, 3, 0), (1, 2, 8), (2, 1, 12)])
+def test_layered_decode_fp32_tiny_shape(pa, first, count, partition):
+    """float32 and blocks of 4 over a layered pool (the vector-ALU kernel, grid
+    over layers, partition merge per layer): max abs error <= 1e-5."""
+    base, pool, q = _tiny_layered("f32", 3)
+    out = pa.decode_layered(to_dev(q[first:first + count]), to_dev(pool),
+                            dev(base.block_tables), dev(base.seq_lens), base.scale,
+                            first_layer=first, partition_size=partition)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle.paged_decode_layered(q, pool, base.block_tables, base.seq_lens, base.scale, 4,
+                                      layers=range(first, first + count))
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - ref).max() <= 1e-5, f"max abs err {np.abs(got - ref).max():.3g}"
+
+
+def test_layered_decode_bf16_blocks_of_four(pa):
+    base, pool, q = _tiny_layered("bf16", 2, seed=22)
+    out = pa.decode_layered(dev(q), dev(pool), dev(base.block_tables), dev(base.seq_lens),
+                            base.scale, partition_size=8)
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode_layered(q, pool, base.block_tables, base.seq_lens, base.scale, 4)
+    assert_close(oracle.to_f64(bits(out)), ref, "bf16 b=4 layered")
+
+
 def test_layered_decode_70b_shape_sampled(pa):
     """64 chat-length sequences of the 70B layer shape, 4 layers in one launch."""
     rng = np.random.default_rng(3)

@@ -36,15 +36,24 @@ def dev(arr):
     return torch.from_numpy(arr).to(DEV)
 
 
+F32_ATOL = 1e-5
+
+
 def host_f64(t):
-    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    t = t.detach().contiguous()
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().astype(np.float64)
+    bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
     return oracle.to_f64(bits)
 
 
-def assert_close(got, ref, what=""):
+def assert_close(got, ref, what="", dtype="bf16"):
     assert got.shape == ref.shape
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max() <= F32_ATOL, f"{what}: max abs err {err.max():.3g}"
+        return
     bad = err > BF16_ATOL + BF16_RTOL * np.abs(ref)
     assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, max abs err {err.max():.3g}"
 
@@ -82,6 +91,28 @@ def test_prefill_ragged_matches_oracle(pa, head_dim, block_size, group):
     assert_close(host_f64(out), oracle_rows(w), f"prefill d={head_dim} b={block_size} G={group}")
 
 
+def test_prefill_tiny_fp32_blocks_of_four(pa):
+    """The tiny decode shape (float32, blocks of 4, table [5, 1, 7]) prefilled
+    on the vector-ALU kernel: whole prompts, a single token and chunks after a
+    cached prefix, every row within 1e-5 of the oracle."""
+    w = W.prefill_tiny_fp32()
+    assert w.block_tables[0, :3].tolist() == [5, 1, 7]
+    out = run(pa, w)
+    assert_close(host_f64(out), oracle_rows(w), "prefill tiny fp32 b=4", "f32")
+
+
+@pytest.mark.parametrize("dtype,block_size,group,head_dim", [
+    ("f32", 4, 4, 64), ("f32", 16, 8, 128), ("f32", 1, 2, 64), ("f32", 32, 1, 128),
+    ("bf16", 4, 4, 64), ("bf16", 8, 8, 128)])
+def test_prefill_vector_alu_shapes(pa, dtype, block_size, group, head_dim):
+    """Shapes the matrix-core prefill does not take (float32, blocks below 16)
+    on the ragged chunk batch, every row against the oracle."""
+    w = W.prefill_tiny(head_dim=head_dim, block_size=block_size, group=group, dtype=dtype)
+    out = run(pa, w)
+    assert_close(host_f64(out), oracle_rows(w), f"prefill {dtype} b={block_size} G={group} "
+                 f"D={head_dim}", dtype)
+
+
 def test_prefill_one_query_chunks_equal_decode(pa):
     """A one-query chunk is a decode query: prefill and decode agree."""
     w = W.prefill_tiny()
@@ -109,10 +140,11 @@ def test_prefill_full_size_every_row(pa, name):
     assert_close(out, ref, name)
 
 
-def test_prefill_unservable_chunks_are_nan(pa):
+@pytest.mark.parametrize("block_size", [16, 4], ids=["matrix-core", "vector-alu"])
+def test_prefill_unservable_chunks_are_nan(pa, block_size):
     """A chunk longer than its sequence, or longer than the host bound, gets
     NaN rows; the other sequences are unaffected."""
-    w = W.prefill_tiny()
+    w = W.prefill_tiny(block_size=block_size)
     ref = oracle_rows(w)
     d = upload(w)
     lens = w.seq_lens.copy()
@@ -131,8 +163,9 @@ def test_prefill_unservable_chunks_are_nan(pa):
     assert_close(out[rest], ref[rest], "chunks within the host bound")
 
 
-def test_prefill_bad_table_entry_poisons_its_sequence(pa):
-    w = W.prefill_tiny()
+@pytest.mark.parametrize("block_size", [16, 4], ids=["matrix-core", "vector-alu"])
+def test_prefill_bad_table_entry_poisons_its_sequence(pa, block_size):
+    w = W.prefill_tiny(block_size=block_size)
     ref = oracle_rows(w)
     d = upload(w)
     bt = w.block_tables.copy()
@@ -145,9 +178,10 @@ def test_prefill_bad_table_entry_poisons_its_sequence(pa):
     assert_close(out[good], ref[good], "other sequences")
 
 
-def test_prefill_skips_sequences_with_offsets_out_of_range(pa):
+@pytest.mark.parametrize("block_size", [16, 4], ids=["matrix-core", "vector-alu"])
+def test_prefill_skips_sequences_with_offsets_out_of_range(pa, block_size):
     """Offsets past num_queries: that sequence's rows are not written."""
-    w = W.prefill_tiny()
+    w = W.prefill_tiny(block_size=block_size)
     ref = oracle_rows(w)
     d = upload(w)
     qs = w.query_start.copy()

@@ -144,6 +144,35 @@ def test_random_prefill(pa, case):
                  f"chunks={chunks.tolist()} lens={lens.tolist()}")
 
 
+@pytest.mark.parametrize("case", range(10 * SCALE))
+def test_random_prefill_vector_alu(pa, case):
+    """Prefill shapes the matrix-core kernel does not take: float32 at any
+    power-of-two block size, bf16 at blocks below 16."""
+    rng = np.random.default_rng([20261202, 5, case])
+    dtype = str(rng.choice(["f32", "bf16"]))
+    head_dim = int(rng.choice([64, 128]))
+    kv_heads = int(rng.integers(1, 4))
+    group = int(rng.choice([1, 2, 4, 8]))
+    block_size = int(rng.choice([1, 2, 4, 8, 16, 32] if dtype == "f32" else [1, 2, 4, 8]))
+    lens = np.maximum(draw_lengths(rng, int(rng.integers(1, 9)), 300), 1)
+    chunks = np.minimum(lens, draw_lengths(rng, len(lens), 120))
+    nb = int(sum(-(-int(n) // block_size) for n in lens)) + 8
+    w = W.build_prefill("random_valu", lens, chunks, dtype=dtype, num_heads=kv_heads * group,
+                        kv_heads=kv_heads, head_dim=head_dim, block_size=block_size,
+                        num_blocks=nb, seed=5000 + case)
+    if w.num_queries == 0:
+        return
+    ref = oracle.paged_prefill(w.q, w.k_cache, w.v_cache, w.block_tables, w.seq_lens,
+                               w.query_lens, w.scale, block_size)
+    out = pa.prefill(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_tables),
+                     dev(w.seq_lens), dev(w.query_start), w.scale,
+                     max_query_len=int(w.query_lens.max()))
+    torch.cuda.synchronize()
+    assert_close(oracle.to_f64(host(out)), ref, dtype,
+                 f"case {case}: {dtype} D={head_dim} Hkv={kv_heads} G={group} b={block_size} "
+                 f"chunks={chunks.tolist()} lens={lens.tolist()}")
+
+
 @pytest.mark.parametrize("case", range(15 * SCALE))
 def test_random_shared_prefix(pa, case):
     rng = np.random.default_rng([20261202, 3, case])

@@ -314,7 +314,7 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
     for (int i = 4 * lane; i < G * D; i += 4 * 64) {
       const int g = i / D;
       const int d = i - g * D;
-      const f32x4 o = *(const f32x4*)&sm_o[wave][g][d];
+      const f32x4 o = *(const f32x4*)&sm_o[wave][g][stash_col<D>(g, d)];
       const float l = sm_l[wave][g];
       if (nparts == 1) {
         const float inv = 1.0f / l;

@@ -266,6 +266,17 @@ __device__ inline void finish_wave(Acc<D>& a, bool bad) {
   }
 }
 
+// Column of head dim d of query-head row g in a merge buffer.  Rows are D
+// floats apart, so the 16 rows' lanes that write one head dim would share an
+// LDS bank; XOR-ing the column with 4 g spreads them over the banks, and
+// keeps every aligned group of four columns together (16-byte reads stay
+// whole).  Measured before the swizzle: 1.8 M bank-conflict cycles per launch
+// on the 70B-shaped batch.
+template <int D>
+__device__ inline int stash_col(int g, int d) {
+  return d ^ ((4 * g) & (D - 1));
+}
+
 // Write one wave's (m, l, O) for query heads g < G into the merge buffers.
 template <int D, int NW>
 __device__ inline void stash_wave(const Acc<D>& a, float (*sm_o)[16][D], float (*sm_m)[16],
@@ -275,7 +286,8 @@ __device__ inline void stash_wave(const Acc<D>& a, float (*sm_o)[16][D], float (
 #pragma unroll
     for (int jt = 0; jt < kVd; ++jt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sm_o[wave][r16][kVd * (4 * q4 + rr) + jt] = a.o[jt][rr];
+      for (int rr = 0; rr < 4; ++rr)
+        sm_o[wave][r16][stash_col<D>(r16, kVd * (4 * q4 + rr) + jt)] = a.o[jt][rr];
     if (q4 == 0) {
       sm_m[wave][r16] = a.m;
       sm_l[wave][r16] = a.l;
@@ -297,7 +309,7 @@ __device__ inline void merge_waves(const float (*sm_o)[16][D], const float (*sm_
   for (int v = 0; v < NW; ++v) {
     const float mv = sm_m[v][g];
     const float wt = mv == -INFINITY ? 0.f : exp2f(mv - mx);
-    o += wt * sm_o[v][g][d];
+    o += wt * sm_o[v][g][stash_col<D>(g, d)];
     l += wt * sm_l[v][g];
   }
 }

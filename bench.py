@@ -73,6 +73,8 @@ def parse():
                          "(pa_decode_shared_prefix)")
     ap.add_argument("--prefix-partition", type=int, default=0,
                     help="shared_prefix: keys per prefix partition (0 = library's choice)")
+    ap.add_argument("--prefill-warmup-ms", type=float, default=300.0,
+                    help="prefill workloads: warm up for at least this long (clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time for cpu_baseline, split over three runs")
@@ -309,14 +311,26 @@ def prefill_main(args, np, torch, W, pa, dev):
         kc, vc = pools[i % len(pools)]
         pa.prefill(q, kc, vc, bt, lens, qs, w.scale, max_query_len=w.max_query_len, out=out)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # The matrix-core prefill is clock-bound, and the clock ramps up over tens
+    # of milliseconds of load after an idle gap (a 50-launch run measured
+    # 392 us for its first timed launch, 334 us for its last).  So the warmup
+    # runs at least `warmup_ms` of launches, and the timed region starts right
+    # after the synchronize, with its events made beforehand.
     timer = HipTimer()
     t_start, t_end = timer.event(), timer.event()
+    step(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step(1)
+    torch.cuda.synchronize()
+    one_ms = max((time.perf_counter() - t0) * 1e3, 1e-3)
+    warm = max(args.warmup, int(args.prefill_warmup_ms / one_ms) + 1)
+    for i in range(warm):
+        step(2 + i)
+    torch.cuda.synchronize()
     timer.record(t_start, stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(2 + warm + i)
     timer.record(t_end, stream)
     torch.cuda.synchronize()
     step_ms = timer.elapsed_ms(t_start, t_end) / args.steps
@@ -348,6 +362,7 @@ def prefill_main(args, np, torch, W, pa, dev):
             "mean_seq_len": round(float(w.seq_lens.mean()), 2),
             "mean_chunk": round(float(w.query_lens.mean()), 2),
             "pool_rotation": len(pools),
+            "warmup_launches": warm + 2,
             "parallelism": "single GPU",
         },
         "flops_per_step": flops,

@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
                                                 "pa_internal.h")],
     "shared_prefix_kernel": [_CSRC + f for f in ("shared_prefix.hip", "decode_mfma.h",
                                                  "row_tiles.h", "mfma_step.h", "pa_internal.h")],
+    "decode_reduce_kernel": [_CSRC + f for f in ("decode_reduce.hip", "pa_internal.h")],
 }
 
 

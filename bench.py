@@ -81,6 +81,9 @@ def parse():
                     help="oracle time for cpu_baseline, split over three runs")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="decode workloads: skip timing the other configs after the headline")
+    ap.add_argument("--power-seconds", type=float, default=0.0,
+                    help="after the measurement, repeat the step for this long while sampling "
+                         "the board's power and graphics clocks (amd-smi); 0 = off")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -106,6 +109,56 @@ def traffic_entry(workload: str, kernel: str = "decode_mfma_kernel"):
     if rec.get("kernel_source_hash") != source_hash(kernel) or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def sample_power(torch, step, seconds):
+    """Repeat `step` for `seconds` while another thread reads the board's
+    socket power and graphics clocks through `amd-smi metric` every ~0.3 s.
+    Reports the medians of the samples taken while the GPU was busy (the
+    first and last samples can straddle the loop's edges), or None when
+    amd-smi is not available."""
+    import shutil
+    import subprocess
+    import threading
+    if seconds <= 0 or shutil.which("amd-smi") is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def reader():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", "0", "--json"],
+                                   capture_output=True, text=True, timeout=20)
+                d = json.loads(r.stdout)
+                d = d[0] if isinstance(d, list) else d
+                d = d["gpu_data"][0] if "gpu_data" in d else d
+                watts = float(d["power"]["socket_power"]["value"])
+                clks = [float(v["clk"]["value"]) for k, v in d["clock"].items()
+                        if k.startswith("gfx_") and isinstance(v, dict)]
+                samples.append((watts, sum(clks) / len(clks) if clks else None))
+            except Exception:  # a malformed or missing reading is skipped
+                pass
+            stop.wait(0.3)
+
+    th = threading.Thread(target=reader, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    busy = samples[1:-1] if len(samples) > 2 else samples
+    if not busy:
+        return None
+    watts = sorted(w for w, _ in busy)
+    clks = sorted(c for _, c in busy if c is not None)
+    return {"socket_power_w": watts[len(watts) // 2],
+            "gfx_clock_mhz": round(clks[len(clks) // 2], 1) if clks else None,
+            "samples": len(busy), "seconds": seconds, "source": "amd-smi metric -p -c"}
 
 
 class HipTimer:
@@ -382,6 +435,8 @@ def prefill_main(args, np, torch, W, pa, dev):
         },
         "cpu_baseline": None,
     }
+    if args.power_seconds > 0:
+        line["power"] = sample_power(torch, lambda i: step(i), args.power_seconds)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = prefill_cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
@@ -854,6 +909,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.power_seconds > 0:
+        line["power"] = sample_power(torch, run.step, args.power_seconds)
     if not args.no_other_configs and args.workload == "llama70b":
         del run
         torch.cuda.empty_cache()

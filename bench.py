@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--rank-in-kernel", action="store_true",
                     help="let every decode work-group rank the batch (pa_decode) instead of "
                          "passing the longest-first order the step keeps (pa_decode_ordered)")
+    ap.add_argument("--index-order", action="store_true",
+                    help="shared_prefix: the tails in index order (pa_decode_shared_prefix) "
+                         "instead of longest first (pa_decode_shared_prefix_ordered)")
     ap.add_argument("--plain-decode", action="store_true",
                     help="shared_prefix: time pa_decode instead of the shared-prefix decode "
                          "(pa_decode_shared_prefix)")
@@ -616,7 +619,7 @@ class DecodeRun:
 
     def __init__(self, np, torch, W, pa, dev, name, *, rotate=4, partition=0, kernel="auto",
                  fused=False, rank_in_kernel=False, plain_decode=False, prefix_partition=0,
-                 host_fill=True):
+                 host_fill=True, index_order=False):
         self.np, self.torch, self.pa, self.W = np, torch, pa, W
         w = self.w = W.make(name, fill=host_fill)
         self.partition, self.kernel, self.prefix_partition = partition, kernel, prefix_partition
@@ -661,6 +664,10 @@ class DecodeRun:
         self.ordered = (not rank_in_kernel and not self.fused and not self.shared
                         and self.plan.kernel == "mfma")
         self.order = pa.longest_first(self.lens) if self.ordered else None
+        # shared-prefix call: the tails' order, longest first, kept like the
+        # decode's order (it changes only with the batch)
+        self.sp_order = (pa.longest_tail_first(self.lens, *self.groups, w.block_size)
+                         if self.shared and not index_order else None)
         self.stream = torch.cuda.current_stream()
 
     def step(self, i, timer=None, ev=None):
@@ -679,7 +686,8 @@ class DecodeRun:
                              w.scale, kernel=self.kernel, **kw)
         elif self.shared:
             pa.decode_shared_prefix(self.q, kc, vc, self.bt, self.lens, w.scale, *self.groups,
-                                    prefix_partition_size=self.prefix_partition, **kw)
+                                    prefix_partition_size=self.prefix_partition,
+                                    order=self.sp_order, **kw)
         elif self.ordered:
             pa.decode_ordered(self.q, kc, vc, self.bt, self.lens, self.order, w.scale,
                               kernel=self.kernel, **kw)
@@ -724,7 +732,8 @@ class DecodeRun:
         dec = float(dec_ms.mean())
         return {
             "workload": self.w.name,
-            "call": ("pa_decode_shared_prefix" if self.shared else
+            "call": ("pa_decode_shared_prefix_ordered" if self.sp_order is not None else
+                     "pa_decode_shared_prefix" if self.shared else
                      "pa_decode_append" if self.fused else
                      "pa_decode_ordered" if self.ordered else "pa_decode"),
             "partition_size": self.plan.partition_size if not self.shared else self.partition,
@@ -823,7 +832,8 @@ def main():
     run = DecodeRun(np, torch, W, pa, dev, args.workload, rotate=args.rotate,
                     partition=args.partition, kernel=args.kernel, fused=args.fused_append,
                     rank_in_kernel=args.rank_in_kernel, plain_decode=args.plain_decode,
-                    prefix_partition=args.prefix_partition, host_fill=True)
+                    prefix_partition=args.prefix_partition, host_fill=True,
+                    index_order=args.index_order)
     w, plan = run.w, run.plan
     step_ms, dec_ms = run.timed(args.steps, args.warmup)
 
@@ -876,9 +886,15 @@ def main():
             "appended_tokens": int(w.slot_mapping.shape[0]),
             "append": "fused into the decode launch" if fused else "pa_kv_append launch",
             "order": ("longest-first, kept across steps (pa_decode_ordered)" if ordered
-                      else "index order (shared-prefix decode)" if shared
+                      else ("tails longest first (pa_decode_shared_prefix_ordered)"
+                            if run.sp_order is not None else "index order (shared-prefix decode)")
+                      if shared
                       else "ranked inside the kernel"),
-            "shared_prefix": ({"call": "pa_decode_shared_prefix", "groups": run.groups[0],
+            "shared_prefix": ({"call": ("pa_decode_shared_prefix" if run.sp_order is None else
+                                        "pa_decode_shared_prefix_ordered"),
+                               "tail_order": ("index" if run.sp_order is None else
+                                              "longest tail first, kept across steps"),
+                               "groups": run.groups[0],
                                "prefix_blocks": run.groups[1],
                                "prefix_partition": args.prefix_partition or "library's choice"}
                               if shared else None),

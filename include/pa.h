@@ -342,6 +342,32 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
                                   void* workspace, size_t workspace_bytes, int32_t dtype,
                                   void* stream);
 
+/*
+ * pa_decode_shared_prefix with the caller's processing order for the tails
+ * (each sequence's positions after its group's prefix): `order` (device int32
+ * [num_seqs]) is a permutation of the sequences, longest tail first.  The
+ * tail work-groups follow the prefix work-groups in one launch and the
+ * hardware dispatches them in index order, so the longest tails first leave
+ * only short ones for the end of the launch (measured on the shared-prefix
+ * workload: 67.7 us per call against 73.1 us in index order).  The order
+ * affects speed only: any permutation gives the same outputs as
+ * pa_decode_shared_prefix, bit for bit.  An entry outside [0, num_seqs)
+ * leaves its tail work item idle, and a sequence missing from `order` gets an
+ * unspecified output row (no memory outside the arrays is touched).  A caller
+ * keeps the order while the batch is unchanged (every decode step adds one
+ * token to every sequence).  NULL order with num_seqs > 0, or an order not
+ * 4-byte aligned -> PA_ERR_INVALID_ARG; otherwise as pa_decode_shared_prefix
+ * (with no group, as pa_decode_ordered with the matrix-core kernel).
+ */
+pa_status pa_decode_shared_prefix_ordered(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    int32_t max_seq_len, const int32_t* order, int32_t num_seqs, int32_t num_heads,
+    int32_t kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    const int32_t* group_start, const int32_t* group_prefix_blocks, int32_t num_groups,
+    int32_t prefix_partition_size, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, int32_t dtype, void* stream);
+
 /* Workspace bytes pa_decode_shared_prefix needs for these arguments (0 when
  * they are invalid or unsupported, or when nothing is shared and the plain
  * decode needs none). */

@@ -144,8 +144,9 @@ __device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_his
 // kModeOrdered: a per-layer pool with the caller's longest-first order.
 // kModeTail: shared-prefix decode; each sequence's partitions start after
 // its group's shared prefix (the prefix work-groups of shared_prefix.hip
-// cover the prefix), in index order, and every partial goes to the
-// workspace unless the sequence has no prefix and one partition.
+// cover the prefix), in the caller's order when one is given (else index
+// order), and every partial goes to the workspace unless the sequence has no
+// prefix and one partition.
 enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered, kModeTail };
 
 // The LDS of one decode work-group, declared by the kernel that runs it (the
@@ -181,8 +182,11 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
     if (rk.seq < 0 || rk.seq >= p.num_seqs) return;
     rk.len = p.seq_lens[rk.seq];
   } else if constexpr (M == kModeTail) {
-    rk.seq = w.seq;
-    rk.len = p.seq_lens[w.seq];
+    // the caller's order (longest tail first) or index order; an entry
+    // outside the batch leaves its slot idle
+    rk.seq = p.order != nullptr ? p.order[w.seq] : w.seq;
+    if (rk.seq < 0 || rk.seq >= p.num_seqs) return;
+    rk.len = p.seq_lens[rk.seq];
   } else {
     rk = ranked_seq(p, w.seq, sm_hist, sm_pick);
   }

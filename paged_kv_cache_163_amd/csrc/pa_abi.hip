@@ -560,16 +560,14 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
                      dtype, kernel, stream, nullptr, nullptr, nullptr);
 }
 
-pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
-                                  const void* v_cache, const int32_t* block_tables,
-                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                  int32_t max_seq_len, int32_t num_seqs, int32_t num_heads,
-                                  int32_t kv_heads, int32_t head_dim, int32_t block_size,
-                                  int32_t num_blocks, float scale, const int32_t* group_start,
-                                  const int32_t* group_prefix_blocks, int32_t num_groups,
-                                  int32_t prefix_partition_size, int32_t partition_size,
-                                  void* workspace, size_t workspace_bytes, int32_t dtype,
-                                  void* stream) {
+static pa_status shared_prefix_impl(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    int32_t max_seq_len, int32_t num_seqs, int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, float scale, const int32_t* group_start,
+    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t prefix_partition_size,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype, void* stream,
+    const int32_t* order) {
   Plan plan;
   pa::PrefixGroups pg;
   const pa_status st = shared_prefix_plan(
@@ -581,7 +579,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
     return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
                        max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
                        num_blocks, scale, partition_size, workspace, workspace_bytes, dtype,
-                       PA_KERNEL_MFMA, stream, nullptr, nullptr, nullptr);
+                       PA_KERNEL_MFMA, stream, nullptr, nullptr, nullptr, nullptr, order);
   // the prefix kernel scales row maxima of raw scores, so scale must be > 0
   if (num_blocks <= 0 || !isfinite(scale) || !(scale > 0.0f)) return PA_ERR_INVALID_ARG;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
@@ -617,9 +615,44 @@ pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
   p.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   p.num_layers = 1;
   p.prefix = pg;
+  p.order = order;
   const hipStream_t s = (hipStream_t)stream;
   if (pa::launch_shared_prefix(p, head_dim, s) != hipSuccess) return PA_ERR_HIP;
   return from_hip(pa::launch_prefix_merge(p, head_dim, s));
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t max_seq_len, int32_t num_seqs, int32_t num_heads,
+                                  int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, const int32_t* group_start,
+                                  const int32_t* group_prefix_blocks, int32_t num_groups,
+                                  int32_t prefix_partition_size, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, int32_t dtype,
+                                  void* stream) {
+  return shared_prefix_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                            max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
+                            num_blocks, scale, group_start, group_prefix_blocks, num_groups,
+                            prefix_partition_size, partition_size, workspace, workspace_bytes,
+                            dtype, stream, nullptr);
+}
+
+pa_status pa_decode_shared_prefix_ordered(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+    int32_t max_seq_len, const int32_t* order, int32_t num_seqs, int32_t num_heads,
+    int32_t kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    const int32_t* group_start, const int32_t* group_prefix_blocks, int32_t num_groups,
+    int32_t prefix_partition_size, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, int32_t dtype, void* stream) {
+  if (order == nullptr && num_seqs > 0) return PA_ERR_INVALID_ARG;
+  if (order != nullptr && !aligned(order, 4)) return PA_ERR_INVALID_ARG;
+  return shared_prefix_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                            max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
+                            num_blocks, scale, group_start, group_prefix_blocks, num_groups,
+                            prefix_partition_size, partition_size, workspace, workspace_bytes,
+                            dtype, stream, order);
 }
 
 size_t pa_decode_shared_prefix_workspace_bytes(

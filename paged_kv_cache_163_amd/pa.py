@@ -74,6 +74,9 @@ _decode_append = _sig("pa_decode_append", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _v
 _decode_shared_prefix = _sig("pa_decode_shared_prefix", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _i32,
                             _i32, _vp, _sz, _i32, _vp)
+_decode_shared_prefix_ordered = _sig("pa_decode_shared_prefix_ordered", _i32, _vp, _vp, _vp, _vp,
+                                    _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _f32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _i32, _vp)
 _shared_prefix_ws = _sig("pa_decode_shared_prefix_workspace_bytes", _sz, _i32, _i32, _i32, _i32,
                          _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32)
 _copy_blocks = _sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
@@ -115,7 +118,8 @@ EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_appe
             "pa_bm_decode_inputs", "pa_bm_sequence", "pa_bm_stats", "pa_bm_refcount",
             "pa_kv_append_layered", "pa_decode_layered", "pa_copy_blocks_layered",
             "pa_swap_blocks_layered", "pa_decode_ordered", "pa_decode_shared_prefix",
-            "pa_decode_shared_prefix_workspace_bytes", "pa_decode_noalloc"]
+            "pa_decode_shared_prefix_workspace_bytes", "pa_decode_noalloc",
+            "pa_decode_shared_prefix_ordered"]
 MAX_PREFIX_GROUPS = 32
 
 
@@ -322,6 +326,19 @@ def longest_first(seq_lens) -> torch.Tensor:
         torch.int32)
 
 
+def longest_tail_first(seq_lens, group_start, group_prefix_blocks, block_size) -> torch.Tensor:
+    """A processing order for decode_shared_prefix(order=...): the sequences by
+    the length of their tail (positions after their group's shared prefix;
+    the whole length outside every group), longest first, stable.  Host
+    helper, int32 on the lengths' device."""
+    gs, gb, n = _host_groups(group_start, group_prefix_blocks)
+    pfx = torch.zeros(seq_lens.shape[0], dtype=torch.int64, device=seq_lens.device)
+    for g in range(n):
+        pfx[int(gs[g]):int(gs[g + 1])] = int(gb[g]) * int(block_size)
+    tails = seq_lens.to(torch.int64) - pfx
+    return torch.sort(tails, descending=True, stable=True).indices.to(torch.int32)
+
+
 def decode_ordered(q, k_cache, v_cache, block_tables, seq_lens, order, scale, max_seq_len=None,
                    partition_size=0, out=None, workspace=None, kernel="auto", stream=None):
     """decode() with a caller-kept processing order (see pa_decode_ordered)."""
@@ -363,13 +380,16 @@ def shared_prefix_workspace_bytes(num_seqs, num_heads, kv_heads, head_dim, block
 
 def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, scale, group_start,
                          group_prefix_blocks, max_seq_len=None, prefix_partition_size=0,
-                         partition_size=0, out=None, workspace=None, stream=None):
+                         partition_size=0, out=None, workspace=None, stream=None, order=None):
     """decode() for a batch whose groups of adjacent sequences share the leading
     blocks of their tables (see pa_decode_shared_prefix).
 
     ``group_start`` (host ints, length num_groups + 1) delimits the groups;
     ``group_prefix_blocks`` (host ints) gives each group's shared leading
-    table entries.  The result equals decode() up to rounding.
+    table entries.  The result equals decode() up to rounding.  ``order``
+    (device int32 [num_seqs], optional): the tails' processing order, a
+    permutation of the sequences with the longest tail first
+    (pa_decode_shared_prefix_ordered; same outputs, faster).
     """
     gs, gb, n = _host_groups(group_start, group_prefix_blocks)
     dt = _dtype_code(q)
@@ -396,13 +416,19 @@ def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, scale, gro
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _decode_shared_prefix(
-        _dev(out, "out", ndim=3), _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
-        _dev(v_cache, "v_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32), maxblk,
-        _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), B, hq, hkv, d, bs, nb,
-        float(scale), gs, gb, n, int(prefix_partition_size), int(partition_size), ws_ptr, ws_len,
-        dt, _stream(stream))
-    _check(st, "decode_shared_prefix")
+    head = (_dev(out, "out", ndim=3), _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
+            _dev(v_cache, "v_cache", ndim=4), _dev(block_tables, "block_tables", torch.int32),
+            maxblk, _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len))
+    tail = (B, hq, hkv, d, bs, nb, float(scale), gs, gb, n, int(prefix_partition_size),
+            int(partition_size), ws_ptr, ws_len, dt, _stream(stream))
+    if order is None:
+        st = _decode_shared_prefix(*head, *tail)
+        _check(st, "decode_shared_prefix")
+    else:
+        if order.dim() != 1 or order.shape[0] != B:
+            raise ValueError("order must be [num_seqs]")
+        st = _decode_shared_prefix_ordered(*head, _dev(order, "order", torch.int32), *tail)
+        _check(st, "decode_shared_prefix_ordered")
     return out
 
 

@@ -339,6 +339,27 @@ def test_shared_prefix_host_validation(built_lib):
     assert call(bs=8, maxblk=300, blocks=[250]) == UNSUPPORTED    # block below a 16-token tile
     assert call(B=0, starts=[0, 0]) == 0                          # empty batch: nothing launched
 
+    # pa_decode_shared_prefix_ordered: the order is checked first, then the
+    # same host validation as the call without it
+    fo = lib.pa_decode_shared_prefix_ordered
+    fo.restype = ctypes.c_int32
+
+    def call_ordered(order, **kw):
+        a = dict(base, **kw)
+        gs, gb, n = arrays(a)
+        return fo(a["out"], a["q"], fake, fake, fake, i32(a["maxblk"]), fake, i32(a["maxlen"]),
+                  order, i32(a["B"]), i32(a["hq"]), i32(a["hkv"]), i32(a["d"]), i32(a["bs"]),
+                  i32(a["nb"]), ctypes.c_float(a["scale"]), gs, gb, i32(n), i32(a["ppart"]),
+                  i32(a["part"]), fake, ctypes.c_size_t(a["ws_bytes"]), i32(a["dt"]), None)
+
+    assert call_ordered(None) == INVALID                          # no order for 216 sequences
+    assert call_ordered(vp(4098)) == INVALID                      # not 4-byte aligned
+    assert call_ordered(None, B=0, starts=[0, 0]) == 0            # empty batch: no order needed
+    for kw, want in (({"starts": [0, 217]}, INVALID), ({"scale": 0.0}, INVALID),
+                     ({"ws_bytes": wsize() - 1}, INVALID), ({"dt": 0}, UNSUPPORTED),
+                     ({"d": 96}, UNSUPPORTED)):
+        assert call_ordered(fake, **kw) == want == call(**kw), kw
+
 
 def test_header_is_c_and_the_library_links_from_c(built_lib, tmp_path):
     """include/pa.h is plain C99 (extern "C" only under C++), and a C program

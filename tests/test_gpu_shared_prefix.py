@@ -192,3 +192,64 @@ def test_shared_prefix_workload_full_size(pa):
     # deterministic
     again = run(pa, d, w, starts, blocks)
     assert torch.equal(again.view(torch.int16), run(pa, d, w, starts, blocks).view(torch.int16))
+
+
+def test_tail_order_changes_speed_only(pa):
+    """pa_decode_shared_prefix_ordered: any permutation of the sequences as
+    the tails' processing order gives the index-order call's output bit for
+    bit (each tail is computed the same way whichever work-group runs it);
+    with no group it is the ordered plain decode."""
+    w, starts, blocks = grouped(LENS, GROUPS, block_size=16, head_dim=128, num_heads=64,
+                                kv_heads=8, seed=5)
+    d = upload(w)
+    B = len(LENS)
+    rng = np.random.default_rng(9)
+    orders = [pa.longest_tail_first(d["lens"], starts, blocks, 16),
+              torch.arange(B - 1, -1, -1, dtype=torch.int32, device=DEV),
+              torch.from_numpy(rng.permutation(B).astype(np.int32)).to(DEV)]
+    for kw in (dict(), dict(prefix_partition_size=32, partition_size=32)):
+        want = run(pa, d, w, starts, blocks, **kw)
+        for order in orders:
+            got = run(pa, d, w, starts, blocks, order=order, **kw)
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (kw, order)
+    plain = pa.decode_ordered(d["q"], d["k"], d["v"], d["bt"], d["lens"], orders[0], w.scale,
+                              max_seq_len=w.max_seq_len, kernel="mfma")
+    out = run(pa, d, w, [0], [], order=orders[0])
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+
+
+def test_tail_order_entry_outside_the_batch_leaves_its_slot_idle(pa):
+    """An order entry outside [0, num_seqs) runs no tail; the sequence it
+    replaced gets an unspecified row, every other row is unchanged."""
+    w, starts, blocks = grouped(LENS, GROUPS, block_size=16, head_dim=128, num_heads=64,
+                                kv_heads=8, seed=6)
+    d = upload(w)
+    want = run(pa, d, w, starts, blocks)
+    order = pa.longest_tail_first(d["lens"], starts, blocks, 16)
+    missing = int(order[3].item())
+    for bad in (-1, len(LENS), 2**31 - 1):
+        o = order.clone()
+        o[3] = bad
+        got = run(pa, d, w, starts, blocks, order=o)
+        keep = [s for s in range(len(LENS)) if s != missing]
+        assert torch.equal(got[keep].view(torch.int16), want[keep].view(torch.int16)), bad
+
+
+def test_shared_prefix_workload_longest_tail_first(pa):
+    """The benchmark's call on the full shared-prefix workload: tails longest
+    first, the same bytes as index order, and within the bar of the oracle on
+    every sequence."""
+    w = W.shared_prefix()
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    oracle.copy_blocks(kc, vc, w.cow_pairs)
+    oracle.kv_append(kc, vc, w.k_new, w.v_new, w.slot_mapping, w.block_size)
+    d = upload(w)
+    pa.copy_blocks(d["k"], d["v"], dev(w.cow_pairs))
+    pa.kv_append(dev(w.k_new), dev(w.v_new), d["k"], d["v"], dev(w.slot_mapping))
+    starts, blocks = [0, w.num_seqs], [w.meta["prefix_blocks"]]
+    order = pa.longest_tail_first(d["lens"], starts, blocks, w.block_size)
+    got = run(pa, d, w, starts, blocks, order=order)
+    want = run(pa, d, w, starts, blocks)
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    ref = oracle.paged_decode(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale, w.block_size)
+    assert_close(as_f64(got), ref, "longest tail first")

@@ -349,9 +349,10 @@ def prefill_cpu_baseline(w, seconds: float):
         "median run reported")
 
 
-def prefill_main(args, np, torch, W, pa, dev):
-    """One step = one pa_prefill launch over the whole batch of chunks."""
-    w = W.PREFILL_WORKLOADS[args.workload]()
+def prefill_timed(np, torch, W, pa, dev, name, steps, warmup, warmup_ms, rotate):
+    """Steady-state pa_prefill timing of workload `name`: (workload, mean
+    launch ms, launches made before the timed region, step function)."""
+    w = W.PREFILL_WORKLOADS[name]()
 
     def to_dev(a):
         a = np.ascontiguousarray(a)
@@ -359,7 +360,7 @@ def prefill_main(args, np, torch, W, pa, dev):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    pools = [(to_dev(w.k_cache), to_dev(w.v_cache)) for _ in range(max(1, args.rotate))]
+    pools = [(to_dev(w.k_cache), to_dev(w.v_cache)) for _ in range(max(1, rotate))]
     q, bt, lens, qs = to_dev(w.q), to_dev(w.block_tables), to_dev(w.seq_lens), to_dev(w.query_start)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
@@ -381,17 +382,33 @@ def prefill_main(args, np, torch, W, pa, dev):
     step(1)
     torch.cuda.synchronize()
     one_ms = max((time.perf_counter() - t0) * 1e3, 1e-3)
-    warm = max(args.warmup, int(args.prefill_warmup_ms / one_ms) + 1)
+    warm = max(warmup, int(warmup_ms / one_ms) + 1)
     for i in range(warm):
         step(2 + i)
     torch.cuda.synchronize()
     timer.record(t_start, stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(2 + warm + i)
     timer.record(t_end, stream)
     torch.cuda.synchronize()
-    step_ms = timer.elapsed_ms(t_start, t_end) / args.steps
+    step_ms = timer.elapsed_ms(t_start, t_end) / steps
     timer.close()
+    return w, step_ms, warm + 2, step
+
+
+def prefill_line(W, w, step_ms):
+    """TFLOP/s, roofline fraction and launch time of one prefill measurement."""
+    flops = W.prefill_flops(w.seq_lens, w.query_lens, w.num_heads, w.head_dim)
+    tflops = flops / (step_ms * 1e-3) / 1e12
+    return {"workload": w.name, "launch_us": round(step_ms * 1e3, 2),
+            "tflops": round(tflops, 2), "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "queries_per_s": round(w.num_queries / (step_ms * 1e-3), 1)}
+
+
+def prefill_main(args, np, torch, W, pa, dev):
+    """One step = one pa_prefill launch over the whole batch of chunks."""
+    w, step_ms, launched, step = prefill_timed(np, torch, W, pa, dev, args.workload, args.steps,
+                                               args.warmup, args.prefill_warmup_ms, args.rotate)
     flops = W.prefill_flops(w.seq_lens, w.query_lens, w.num_heads, w.head_dim)
     tflops = flops / (step_ms * 1e-3) / 1e12
     kv_bytes = W.decode_kv_bytes(w.seq_lens, w.kv_heads, w.head_dim, w.elem_bytes)
@@ -418,8 +435,8 @@ def prefill_main(args, np, torch, W, pa, dev):
             "block_size": w.block_size,
             "mean_seq_len": round(float(w.seq_lens.mean()), 2),
             "mean_chunk": round(float(w.query_lens.mean()), 2),
-            "pool_rotation": len(pools),
-            "warmup_launches": warm + 2,
+            "pool_rotation": max(1, args.rotate),
+            "warmup_launches": launched,
             "parallelism": "single GPU",
         },
         "flops_per_step": flops,
@@ -940,6 +957,13 @@ def main():
         others, paging = other_configs(np, torch, W, pa, dev)
         line["other_configs"] = others
         line["paging_overhead"] = paging
+        # the two prefill batches, steady state (each warms up for 300 ms first)
+        pf = []
+        for name in ("prefill_llama70b", "prefill_chunked"):
+            w_p, ms_p, _, _ = prefill_timed(np, torch, W, pa, dev, name, 100, 10, 300.0, 4)
+            pf.append(prefill_line(W, w_p, ms_p))
+            torch.cuda.empty_cache()
+        line["prefill"] = pf
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -790,10 +790,10 @@ def other_configs(np, torch, W, pa, dev, steps=40, warmup=20):
     the paging overhead: the llama70b batch against the same batch on
     physically consecutive blocks, in alternating rounds.  The pools are the
     workloads' seeded host-filled ones, copied to the device like the
-    headline's: fresh device-filled pools of the same shape measured up to 4 %
-    slower (the contents do not matter: refilling the same allocations with
-    random, zero or the seeded values gives the same times; the allocations
-    themselves differ)."""
+    headline's.  (Pools allocated after earlier pools were freed have
+    measured up to 4 % slower whatever their contents or allocation call, so
+    the measured speed of a config depends a little on what the process
+    allocated before it.)"""
     res = []
     for name, part, note in OTHER_CONFIGS:
         run = DecodeRun(np, torch, W, pa, dev, name, partition=part, host_fill=True)

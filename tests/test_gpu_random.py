@@ -209,6 +209,14 @@ def test_random_shared_prefix(pa, case):
     assert_close(oracle.to_f64(host(out)), ref, "bf16",
                  f"case {case}: D={head_dim} Hkv={kv_heads} G={group} b={block_size} "
                  f"groups={bounds} prefix={prefix} P={ppart}")
+    # the tails in a random order: the same bytes
+    order = torch.from_numpy(rng.permutation(B).astype(np.int32)).to(DEV)
+    again = pa.decode_shared_prefix(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(bt),
+                                    dev(w.seq_lens), w.scale, bounds, prefix,
+                                    max_seq_len=w.max_seq_len, prefix_partition_size=ppart,
+                                    order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), out.view(torch.int16)), f"case {case}: order"
 
 
 @pytest.mark.parametrize("case", range(20 * SCALE))

@@ -779,6 +779,7 @@ OTHER_CONFIGS = [
     ("shared_prefix", 0, "pa_decode_shared_prefix, library's split"),
     ("long_context", 512, "16 partitions of 512 tokens + reduce"),
     ("long_context", 0, "library's split"),
+    ("llama70b_tp8", 0, "one GPU's share at 8-way tensor parallelism: 1 KV head, 8 query heads"),
     *[(W_name, 0, "append + decode") for W_name in
       ("sweep_b16_d64", "sweep_b16_d128", "sweep_b32_d64", "sweep_b32_d128",
        "sweep_b64_d64", "sweep_b64_d128")],

@@ -365,23 +365,36 @@ def tiny(seed: int = 0, append: bool = True, fill: bool = True) -> DecodeWorkloa
 
 
 def llama70b(seed: int = 0, num_seqs: int = 256, append: bool = True,
-             sequential: bool = False, fill: bool = True) -> DecodeWorkload:
+             sequential: bool = False, fill: bool = True, tp: int = 1) -> DecodeWorkload:
     """One Llama-3.1-70B-shaped layer: 256 chat sequences, bf16, b=16, 20k blocks
-    (``sequential``: the same batch on physically consecutive blocks)."""
+    (``sequential``: the same batch on physically consecutive blocks; ``tp``:
+    one GPU's share under tensor parallelism over ``tp`` GPUs, 8/tp KV heads
+    and 64/tp query heads of every block, the same lengths and placement)."""
+    if tp not in (1, 2, 4, 8):
+        raise ValueError("tp must divide the 8 KV heads")
     rng = np.random.default_rng(seed)
     prompt = rng.integers(500, 700, size=num_seqs, endpoint=True)
     generated = rng.integers(0, 250, size=num_seqs, endpoint=True)
+    name = "llama70b_contiguous" if sequential else "llama70b"
+    if tp > 1:
+        name += f"_tp{tp}"
     return build_private(
-        "llama70b_contiguous" if sequential else "llama70b", prompt + generated, dtype="bf16",
-        num_heads=64, kv_heads=8, head_dim=128, block_size=16, num_blocks=20000, append=append,
-        rng=rng, seed=seed, sequential=sequential, fill=fill,
+        name, prompt + generated, dtype="bf16",
+        num_heads=64 // tp, kv_heads=8 // tp, head_dim=128, block_size=16, num_blocks=20000,
+        append=append, rng=rng, seed=seed, sequential=sequential, fill=fill,
         meta={"prompt": "U{500..700}", "generated": "U{0..250}",
-              "placement": "sequential" if sequential else "random"})
+              "placement": "sequential" if sequential else "random", "tp": tp})
 
 
 def llama70b_contiguous(seed: int = 0, fill: bool = True) -> DecodeWorkload:
     """The llama70b batch with each sequence's blocks physically consecutive."""
     return llama70b(seed=seed, sequential=True, fill=fill)
+
+
+def llama70b_tp8(seed: int = 0, fill: bool = True) -> DecodeWorkload:
+    """One GPU's share of the llama70b batch under 8-way tensor parallelism:
+    one KV head and its 8 query heads of every block, the same lengths."""
+    return llama70b(seed=seed, fill=fill, tp=8)
 
 
 def long_context(seed: int = 0, fill: bool = True) -> DecodeWorkload:
@@ -635,6 +648,7 @@ WORKLOADS = {
     "shared_prefix": shared_prefix,
     "long_context": long_context,
     "llama70b_contiguous": llama70b_contiguous,
+    "llama70b_tp8": llama70b_tp8,
 }
 
 

@@ -75,6 +75,14 @@ def test_decode_plan(pa):
     assert pa.decode_plan(64, 64, 8, 128, 16, 8192, kernel="mfma").num_partitions == 1
     # 256 (sequence, head) pairs fill the GPU for the split kernel: no split
     assert pa.decode_plan(256, 64, 8, 128, 16, 951, kernel="mfma").num_partitions == 1
+    # no partition shorter than 1,024 tokens: one KV head of 256 chats of up
+    # to 950 tokens (256 pairs) stays whole, the same pairs at 8,192 tokens
+    # take 2 partitions (512 work-groups), and 64 pairs of 3,000 tokens take
+    # 2 of 1,504 rather than 8 of 375
+    assert pa.decode_plan(256, 8, 1, 128, 16, 950, kernel="mfma").num_partitions == 1
+    assert tuple(pa.decode_plan(256, 8, 1, 128, 16, 8192, kernel="mfma")[1:3]) == (4096, 2)
+    assert tuple(pa.decode_plan(64, 8, 1, 128, 16, 3000, kernel="mfma")[1:3]) == (1504, 2)
+    assert pa.decode_plan(16, 64, 8, 128, 16, 1023, kernel="mfma").num_partitions == 1
     # the matrix-core split kernel rounds partitions to whole 32-token steps
     assert pa.decode_plan(4, 8, 2, 64, 16, 100, partition_size=8, dtype=torch.bfloat16,
                           kernel="mfma").partition_size == 32

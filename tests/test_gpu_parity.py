@@ -296,6 +296,23 @@ def test_llama70b_full(pa):
     assert_close(as_f64(o), ref, "bf16", "llama70b valu")
 
 
+def test_llama70b_tp8_share_full(pa):
+    """One GPU's share of the llama70b batch under 8-way tensor parallelism
+    (one KV head, 8 query heads; 256 (sequence, KV head) pairs, so the plan
+    splits the sequences): the step and the benchmark's ordered launch on
+    every sequence against the oracle."""
+    w = W.llama70b_tp8()
+    d, out, kc, vc, ref = _full_step_and_decode(pa, w)
+    plan = pa.decode_plan(w.num_seqs, w.num_heads, w.kv_heads, w.head_dim, w.block_size,
+                          w.max_seq_len, 0, torch.bfloat16, "auto")
+    assert plan.kernel == "mfma"
+    o = pa.decode_ordered(d["q"], d["k"], d["v"], d["bt"], d["lens"], pa.longest_first(d["lens"]),
+                          w.scale, max_seq_len=w.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), out.view(torch.int16))
+    assert_close(as_f64(o), ref, "bf16", "llama70b tp8 share, decode_ordered")
+
+
 def test_contiguous_placement_gives_the_same_bytes(pa):
     """The llama70b batch on physically consecutive blocks holds the same
     logical K/V as the randomly placed one: the decode (the benchmark's

@@ -1,6 +1,7 @@
 """The measurement harness on the CPU: bench.py's multi-GPU refusal, the
 counter records it trusts only while the kernel sources are unchanged, and the
-rocprofv3 summaries of paged_kv_cache_163_amd/profiling.py on synthetic CSVs."""
+rocprofv3 summaries of paged_kv_cache_163_amd/profiling.py on synthetic CSVs, and
+the power sampler on a stand-in amd-smi."""
 
 import csv
 import json
@@ -97,3 +98,38 @@ def test_cpu_baseline_summary_takes_the_median_run_and_measured_cores():
     assert res["cores"] == 4
     assert {"vendor", "threads"} <= set(res["blas"]) and res["affinity_cpus"] >= 1
     assert res["kind"] == "oracle"
+
+
+class _FakeCuda:
+    @staticmethod
+    def synchronize():
+        pass
+
+
+class _FakeTorch:
+    cuda = _FakeCuda()
+
+
+def test_power_sampler_reads_amd_smi_json(tmp_path, monkeypatch):
+    """bench.sample_power runs the step while a thread reads `amd-smi metric
+    -p -c --json`: medians of socket power and of the mean graphics clock over
+    the samples taken while busy; None without amd-smi."""
+    import bench
+    fake = tmp_path / "amd-smi"
+    reading = {"gpu_data": [{"gpu": 0,
+                             "power": {"socket_power": {"value": 1390, "unit": "W"}},
+                             "clock": {"gfx_0": {"clk": {"value": 2200, "unit": "MHz"}},
+                                       "gfx_1": {"clk": {"value": 2300, "unit": "MHz"}},
+                                       "mem_0": {"clk": {"value": 1900, "unit": "MHz"}}}}]}
+    fake.write_text("#!/bin/sh\ncat <<'JSON'\n" + json.dumps(reading) + "\nJSON\n")
+    fake.chmod(0o755)
+    monkeypatch.setenv("PATH", str(tmp_path) + os.pathsep + os.environ.get("PATH", ""))
+    calls = []
+    res = bench.sample_power(_FakeTorch, lambda i: calls.append(i), 1.0)
+    assert res is not None and calls
+    assert res["socket_power_w"] == 1390.0
+    assert res["gfx_clock_mhz"] == 2250.0          # mean of the graphics clocks only
+    assert res["samples"] >= 1
+    monkeypatch.setenv("PATH", str(tmp_path / "nowhere"))
+    assert bench.sample_power(_FakeTorch, lambda i: None, 1.0) is None
+    assert bench.sample_power(_FakeTorch, lambda i: None, 0.0) is None

@@ -678,7 +678,7 @@ class DecodeRun:
                 w.max_blocks_per_seq, *self.groups, prefix_partition_size=prefix_partition,
                 partition_size=partition)
         self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-        self.ordered = (not rank_in_kernel and not self.fused and not self.shared
+        self.ordered = (not rank_in_kernel and not self.shared
                         and self.plan.kernel == "mfma")
         self.order = pa.longest_first(self.lens) if self.ordered else None
         # shared-prefix call: the tails' order, longest first, kept like the
@@ -700,7 +700,7 @@ class DecodeRun:
                   workspace=self.ws)
         if self.fused:   # one launch: the new tokens' append and the decode
             pa.decode_append(self.q, kc, vc, self.fk, self.fv, self.fslots, self.bt, self.lens,
-                             w.scale, kernel=self.kernel, **kw)
+                             w.scale, kernel=self.kernel, order=self.order, **kw)
         elif self.shared:
             pa.decode_shared_prefix(self.q, kc, vc, self.bt, self.lens, w.scale, *self.groups,
                                     prefix_partition_size=self.prefix_partition,
@@ -768,7 +768,8 @@ class DecodeRun:
             "workload": self.w.name,
             "call": ("pa_decode_shared_prefix_ordered" if self.sp_order is not None else
                      "pa_decode_shared_prefix" if self.shared else
-                     "pa_decode_append" if self.fused else
+                     ("pa_decode_append_ordered" if self.ordered else "pa_decode_append")
+                     if self.fused else
                      "pa_decode_ordered" if self.ordered else "pa_decode"),
             "partition_size": self.plan.partition_size if not self.shared else self.partition,
             "num_partitions": self.plan.num_partitions,

@@ -259,8 +259,9 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
  * sequence's blocks).  Same result as
  *     pa_kv_append(k_new, v_new, k_cache, v_cache, slot_mapping, num_seqs, ...)
  *     pa_decode(out, q, k_cache, v_cache, block_tables, ..., seq_lens, ...)
- * (bit-identical cache; decode outputs equal up to the rounding of the
- * chosen kernel), without the second launch.
+ * (bit-identical cache; bit-identical outputs when the decode runs the same
+ * kernel shape: pa_decode_plan's choice unless it splits partitions per
+ * wave, which the fused call does not), without the second launch.
  *
  *   k_new, v_new   [num_seqs][kv_heads][head_dim], dtype: sequence s's new token
  *   slot_mapping   int64 [num_seqs]: cache slot of sequence s's new token, or
@@ -268,16 +269,14 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
  *   seq_lens       lengths AFTER the append; when slot_mapping[s] >= 0 the new
  *                  token is position seq_lens[s] - 1, and slot_mapping[s] must
  *                  be that position's slot under the sequence's block table
- * The new token's score and value come from k_new/v_new.  The matrix-core
- * kernel's loads of the last tile may still read the slot being written
- * (by another work-group of the same launch), but that position is masked
- * out of the step math before its value is used, so the result never
- * depends on what the read returns.  The slot's block must not be read by
- * any other sequence in the same call (copy-on-write first).
- * Other arguments, errors and shapes as pa_decode_ex.  On the 70B-shaped
- * batch one launch measured a little slower than pa_kv_append + pa_decode
- * (the owning work-group folds the new token in serially after its step
- * loop).
+ * The new token's K and V come from k_new/v_new: the work-group whose
+ * partition holds the token (the sequence's last one) loads the token's tile
+ * from the cache as usual and replaces that row with the new rows in
+ * registers before the step's math, then writes the rows to the slot after
+ * its last cache read.  No other work-group reads the slot.  The slot's
+ * block must not be read by any other sequence in the same call
+ * (copy-on-write first).  Other arguments, errors and shapes as
+ * pa_decode_ex.
  */
 pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache,
                            const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -287,6 +286,27 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
                            int32_t block_size, int32_t num_blocks, float scale,
                            int32_t partition_size, void* workspace, size_t workspace_bytes,
                            int32_t dtype, int32_t kernel, void* stream);
+
+/*
+ * pa_decode_append with the work-groups dispatched in the caller's order, as
+ * pa_decode_ordered does for pa_decode (same `order` argument: a permutation
+ * of the batch, longest sequence first for speed; it changes only the
+ * dispatch order, never a result).  An entry outside [0, num_seqs) leaves its
+ * work-group idle, so a sequence missing from `order` gets neither its
+ * output row nor its append.  A null `order` (with num_seqs > 0) ->
+ * PA_ERR_INVALID_ARG; everything else as pa_decode_append.  On the 70B-shaped
+ * batch this one launch is the decode step (append and decode).
+ */
+pa_status pa_decode_append_ordered(void* out, const void* q, void* k_cache, void* v_cache,
+                                   const void* k_new, const void* v_new,
+                                   const int64_t* slot_mapping, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   int32_t max_seq_len, const int32_t* order, int32_t num_seqs,
+                                   int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, float scale,
+                                   int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, int32_t dtype, int32_t kernel,
+                                   void* stream);
 
 /*
  * Shared-prefix decode: the result of pa_decode for a batch in which groups of

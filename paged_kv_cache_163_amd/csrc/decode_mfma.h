@@ -142,12 +142,13 @@ __device__ inline Ranked ranked_seq(const DecodeParams& p, int slot, int* sm_his
 // kModePlain: one per-layer pool.  kModeFused: plus the step's append.
 // kModeLayered: one or more layers of a layered pool (layer = blockIdx.y).
 // kModeOrdered: a per-layer pool with the caller's longest-first order.
+// kModeFusedOrdered: kModeFused in the caller's order.
 // kModeTail: shared-prefix decode; each sequence's partitions start after
 // its group's shared prefix (the prefix work-groups of shared_prefix.hip
 // cover the prefix), in the caller's order when one is given (else index
 // order), and every partial goes to the workspace unless the sequence has no
 // prefix and one partition.
-enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered, kModeTail };
+enum Mode { kModePlain, kModeFused, kModeLayered, kModeOrdered, kModeTail, kModeFusedOrdered };
 
 // The LDS of one decode work-group, declared by the kernel that runs it (the
 // shared-prefix launch overlays it with the prefix work-groups' staging).
@@ -166,7 +167,7 @@ struct DecodeLds {
 template <int D, int M, int NW = kWaves, bool WP = false>
 __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeLds<D, NW>& lds) {
   constexpr int kKi = D / 32;
-  constexpr bool kFused = M == kModeFused;
+  constexpr bool kFused = M == kModeFused || M == kModeFusedOrdered;
   static_assert(!(WP && (kFused || M == kModeTail)), "wave-per-partition: plain modes only");
   auto& sm_o = lds.o;
   auto& sm_m = lds.m;
@@ -176,7 +177,7 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
   unsigned char* sm_new = lds.nw;
   WorkItem w = decode_work_item(p, wg);
   Ranked rk;
-  if constexpr (M == kModeOrdered) {
+  if constexpr (M == kModeOrdered || M == kModeFusedOrdered) {
     // the caller's order; an entry outside the batch leaves its slot idle
     rk.seq = p.order[w.seq];
     if (rk.seq < 0 || rk.seq >= p.num_seqs) return;
@@ -238,23 +239,27 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
   const int pstart = (int)pstart64;
   const int pend = range_end(pstart, p.partition_size, len);
   const int nparts = ceil_div_i(len - pfx, p.partition_size);
-  // Fused append: the partition that holds the new token (position len - 1,
-  // so the last one) masks it out of the step math and folds it in from the
-  // new row afterwards; partition 0 writes it to its cache slot at the very
-  // end.  Both fetch the slot and the row (wave 0 lanes only) up front, so
-  // neither waits on memory after the loop.
+  // Fused append: the new token is position len - 1, in the last partition.
+  // Its work-group takes the token's K and V from the new rows instead of the
+  // cache slot (patched into the loaded step, before its math, by the wave
+  // whose step holds the token), so the decode is exactly the plain decode of
+  // the appended cache; that wave writes the rows to the slot after its last
+  // cache read.  It fetches the rows (lanes 0 .. kNewParts-1) up front and
+  // keeps them in LDS (sm_new, its own) rather than in registers.
   constexpr int kNewParts = D / 4;  // 16-byte parts of the K and V rows
-  bool own_new = false;
-  int pend_loop = pend;
+  int new_pos = -1;                 // the new token's position, if in this partition
+  int new_wave = -1;                // the wave whose step holds it
   int64_t new_slot = -1;
   nt_u32x4 new_part = {0u, 0u, 0u, 0u};
   if constexpr (kFused) {
-    if ((pend == len || w.part == 0) && tid < kNewParts)
-      new_part = new_row_part(p, w.seq, w.head, D * 2, tid);
     const NewToken nt = new_token(p, w.seq, w.head, len, D * 2);
-    new_slot = nt.slot;
-    own_new = nt.pos >= pstart && nt.pos < pend;
-    if (own_new) pend_loop = nt.pos;
+    if (nt.pos >= pstart && nt.pos < pend) {
+      new_pos = nt.pos;
+      new_slot = nt.slot;
+      new_wave = ((nt.pos - pstart) >> 5) % NW;
+      if (wave == new_wave && lane < kNewParts)
+        new_part = new_row_part(p, w.seq, w.head, D * 2, lane);
+    }
   }
 
   // Q^T as the B operand: column r16 = query head h*G + r16, zero when r16 >= G.
@@ -281,32 +286,30 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
   reset(a);
   bool bad = false;
 
-  // Two register sets, loads one step ahead of the math.  Loads and the loop
-  // run to pend; the math masks from pend_loop, which in fused mode stops one
-  // token short in the owning partition (so no load waits for the new-token
-  // slot, and a wave may meet a step that is wholly masked).
+  // Two register sets, loads one step ahead of the math; tokens >= pend masked.
   const int stride = WP ? 32 : 32 * NW;
   int base = WP ? pstart : pstart + 32 * wave;
   if (base < pend) {
     StepRegs<D> ra, rb;
     load_step<D>(ra, c, base, r16, q4, bad);
+    if (kFused && wave == new_wave && lane < kNewParts)
+      *(nt_u32x4*)(sm_new + 16 * lane) = new_part;
     while (true) {
       int next = base + stride;
       if (next < pend) load_step<D>(rb, c, next, r16, q4, bad);
-      compute_step<D, kFused>(ra, a, qb, base, pend_loop, p.scale_log2, q4);
+      if (kFused && wave == new_wave && new_pos >= base && new_pos < base + 32)
+        patch_new_token<D>(ra, sm_new, new_pos - base, r16, q4);
+      compute_step<D>(ra, a, qb, base, pend, p.scale_log2, q4);
       base = next;
       if (base >= pend) break;
       next = base + stride;
       if (next < pend) load_step<D>(ra, c, next, r16, q4, bad);
-      compute_step<D, kFused>(rb, a, qb, base, pend_loop, p.scale_log2, q4);
+      if (kFused && wave == new_wave && new_pos >= base && new_pos < base + 32)
+        patch_new_token<D>(rb, sm_new, new_pos - base, r16, q4);
+      compute_step<D>(rb, a, qb, base, pend, p.scale_log2, q4);
       base = next;
       if (base >= pend) break;
     }
-  }
-  if (kFused && own_new && wave == 0) {
-    if (tid < kNewParts) *(nt_u32x4*)(sm_new + 16 * tid) = new_part;
-    __builtin_amdgcn_wave_barrier();  // one wave: its LDS operations run in order
-    add_token<D>(a, qb, sm_new, sm_new + D * 2, p.scale_log2, r16, q4);
   }
   finish_wave(a, bad);
   stash_wave<D, NW>(a, sm_o, sm_m, sm_l, wave, r16, q4, G);
@@ -354,7 +357,8 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, int wg, DecodeL
       }
     }
   }
-  if (kFused && w.part == 0) store_row_part(p, new_slot, w.head, D * 2, tid, new_part);
+  if (kFused && wave == new_wave && lane < kNewParts)
+    store_row_part(p, new_slot, w.head, D * 2, lane, *(const nt_u32x4*)(sm_new + 16 * lane));
 }
 
 }  // namespace

@@ -29,14 +29,21 @@ hipError_t launch_nw(const DecodeParams& p, int mode, dim3 grid, hipStream_t str
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, int mode, dim3 grid, hipStream_t stream) {
-  if (mode == kModeFused) {  // the fused append keeps one partition per work-group
+  if (mode == kModeFused || mode == kModeFusedOrdered) {
+    // the fused append keeps one partition per work-group
     const dim3 block(p.waves * 64);
-    if (p.waves == 4 && !p.wave_parts)
-      decode_mfma_kernel<D, kModeFused, 4, false><<<grid, block, 0, stream>>>(p);
-    else if (p.waves == 2 && !p.wave_parts)
-      decode_mfma_kernel<D, kModeFused, 2, false><<<grid, block, 0, stream>>>(p);
-    else
-      return hipErrorInvalidValue;
+    if (p.wave_parts || (p.waves != 4 && p.waves != 2)) return hipErrorInvalidValue;
+    if (mode == kModeFused) {
+      if (p.waves == 4)
+        decode_mfma_kernel<D, kModeFused, 4, false><<<grid, block, 0, stream>>>(p);
+      else
+        decode_mfma_kernel<D, kModeFused, 2, false><<<grid, block, 0, stream>>>(p);
+    } else {
+      if (p.waves == 4)
+        decode_mfma_kernel<D, kModeFusedOrdered, 4, false><<<grid, block, 0, stream>>>(p);
+      else
+        decode_mfma_kernel<D, kModeFusedOrdered, 2, false><<<grid, block, 0, stream>>>(p);
+    }
     return hipGetLastError();
   }
   if (p.wave_parts) {
@@ -59,7 +66,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, hipStream_t s
   const dim3 grid((unsigned)(groups * p.num_seqs * p.kv_heads),
                   (unsigned)(p.num_layers > 1 ? p.num_layers : 1));
   const int mode = p.block_stride != 0     ? kModeLayered
-                   : p.new_slots != nullptr ? kModeFused
+                   : p.new_slots != nullptr ? (p.order != nullptr ? kModeFusedOrdered : kModeFused)
                    : p.order != nullptr     ? kModeOrdered
                                             : kModePlain;
   if (head_dim == 128) return launch_d<128>(p, mode, grid, stream);

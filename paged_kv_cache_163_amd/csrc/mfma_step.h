@@ -214,44 +214,33 @@ __device__ inline void compute_step(StepRegs<D>& r, Acc<D>& a, const u32x4* qb, 
   }
 }
 
-// Fold one extra token into a wave's running state: the fused append's new
-// token, whose K and V rows (bf16, head_dim values each) are staged in LDS.
-// The score is reduced from each lane's share of the head dimension (the same
-// d set its Q operand holds), and the probability is rounded to bf16 exactly
-// as in compute_step, so the result matches reading the token from the cache.
+// Fused append: in a loaded step, replace the operands of the token at
+// offset `off` (0..31) of the step by that token's new K and V rows, staged
+// in `sm` (the K row, then the V row; LDS that only the calling wave writes):
+// K row 16*kt + r16 at bytes 64*i + 16*q4 (load_step), V row 16*(e/4) +
+// 4*q4 + e%4 at bytes (D/16)*2*r16.  The step's math is then that of the
+// appended cache.
 template <int D>
-__device__ inline void add_token(Acc<D>& a, const u32x4* qb, const unsigned char* krow,
-                                 const unsigned char* vrow, float scale_log2, int r16, int q4) {
-  constexpr int kKi = D / 32;
-  constexpr int kVd = D / 16;
-  float part = 0.f;
+__device__ inline void patch_new_token(StepRegs<D>& r, const unsigned char* sm, int off, int r16,
+                                       int q4) {
+  using VT = typename VRow<D>::T;
+  const int kt_new = off >> 4;
+  const int rr = off & 15;
 #pragma unroll
-  for (int i = 0; i < kKi; ++i) {
-    const u32x4 kk = *(const u32x4*)(krow + 64 * i + 16 * q4);
+  for (int kt = 0; kt < 2; ++kt) {
+    if (kt == kt_new) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      part = fmaf(bf16_lo(qb[i][w]), bf16_lo(kk[w]), part);
-      part = fmaf(bf16_hi(qb[i][w]), bf16_hi(kk[w]), part);
+      for (int i = 0; i < D / 32; ++i) {
+        const u32x4 v = *(const u32x4*)(sm + 64 * i + 16 * q4);
+        r.k[kt][i] = r16 == rr ? v : r.k[kt][i];
+      }
     }
   }
-  part += __shfl_xor(part, 16);
-  part += __shfl_xor(part, 32);
-  const float s = part * scale_log2;
-  const float m_new = fmaxf(a.m, s);
-  const float keep = __builtin_amdgcn_exp2f(a.m - m_new);
-  const uint32_t pbits = f32_to_bf16(__builtin_amdgcn_exp2f(s - m_new));
-  const float pr = __uint_as_float(pbits << 16);
-  a.l = a.l * keep + (q4 == 0 ? pr : 0.f);  // one share per r16
-  a.m = m_new;
+  const int e_new = 4 * kt_new + (rr & 3);
+  const VT v = *(const VT*)(sm + D * 2 + (D / 16) * 2 * r16);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const typename VRow<D>::T vv = *(const typename VRow<D>::T*)(vrow + (kVd * (4 * q4 + r)) * 2);
-#pragma unroll
-    for (int jt = 0; jt < kVd; ++jt) {
-      const float v = (jt & 1) ? bf16_hi(vv[jt >> 1]) : bf16_lo(vv[jt >> 1]);
-      a.o[jt][r] = fmaf(pr, v, a.o[jt][r] * keep);
-    }
-  }
+  for (int e = 0; e < 8; ++e)
+    if (e == e_new) r.v[e] = q4 == (rr >> 2) ? v : r.v[e];
 }
 
 // Finish a wave's running sum (the four lanes of each r16 hold shares).

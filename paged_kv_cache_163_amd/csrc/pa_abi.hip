@@ -382,7 +382,7 @@ static pa_status decode_impl(void* out, const void* q, const void* k_cache, cons
   }
   if (order != nullptr) {
     if (!aligned(order, 4)) return PA_ERR_INVALID_ARG;
-    if (plan.kernel == PA_KERNEL_MFMA && !fused) p.order = order;  // others rank nothing
+    if (plan.kernel == PA_KERNEL_MFMA) p.order = order;  // the vector-ALU kernel ranks nothing
   }
   if (lay != nullptr) {
     p.block_stride = lay->block_stride;
@@ -533,6 +533,24 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
                      max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
                      num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, kernel,
                      stream, k_new, v_new, num_seqs > 0 ? slot_mapping : nullptr);
+}
+
+pa_status pa_decode_append_ordered(void* out, const void* q, void* k_cache, void* v_cache,
+                                   const void* k_new, const void* v_new,
+                                   const int64_t* slot_mapping, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   int32_t max_seq_len, const int32_t* order, int32_t num_seqs,
+                                   int32_t num_heads, int32_t kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, float scale,
+                                   int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, int32_t dtype, int32_t kernel,
+                                   void* stream) {
+  if (num_seqs > 0 && (slot_mapping == nullptr || order == nullptr)) return PA_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+                     max_seq_len, num_seqs, num_heads, kv_heads, head_dim, block_size,
+                     num_blocks, scale, partition_size, workspace, workspace_bytes, dtype, kernel,
+                     stream, k_new, v_new, num_seqs > 0 ? slot_mapping : nullptr, nullptr,
+                     order);
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

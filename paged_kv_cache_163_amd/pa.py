@@ -71,6 +71,9 @@ _decode_ordered = _sig("pa_decode_ordered", _i32, _vp, _vp, _vp, _vp, _vp, _i32,
 _decode_append = _sig("pa_decode_append", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32,
                       _vp)
+_decode_append_ordered = _sig("pa_decode_append_ordered", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                              _i32, _vp, _sz, _i32, _i32, _vp)
 _decode_shared_prefix = _sig("pa_decode_shared_prefix", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _i32, _i32,
                             _i32, _vp, _sz, _i32, _vp)
@@ -119,7 +122,7 @@ EXPORTED = ["pa_abi_version", "pa_status_string", "pa_block_layout", "pa_kv_appe
             "pa_kv_append_layered", "pa_decode_layered", "pa_copy_blocks_layered",
             "pa_swap_blocks_layered", "pa_decode_ordered", "pa_decode_shared_prefix",
             "pa_decode_shared_prefix_workspace_bytes", "pa_decode_noalloc",
-            "pa_decode_shared_prefix_ordered"]
+            "pa_decode_shared_prefix_ordered", "pa_decode_append_ordered"]
 MAX_PREFIX_GROUPS = 32
 
 
@@ -434,12 +437,13 @@ def decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, scale, gro
 
 def decode_append(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_tables, seq_lens, scale,
                   max_seq_len=None, partition_size=0, out=None, workspace=None, kernel="auto",
-                  stream=None):
+                  stream=None, order=None):
     """Fused decode step: append one new token per sequence, then decode.
 
     ``k_new``/``v_new`` are [num_seqs, kv_heads, head_dim]; ``slot_mapping``
     int64 [num_seqs] (< 0: no new token for that sequence); ``seq_lens`` are
     the lengths after the append.  Same result as ``kv_append`` + ``decode``.
+    With ``order`` (see longest_first) the call is pa_decode_append_ordered.
     """
     B = q.shape[0]
     if k_new.shape != (B, k_cache.shape[1], q.shape[2]) or v_new.shape != k_new.shape:
@@ -451,12 +455,21 @@ def decode_append(q, k_cache, v_cache, k_new, v_new, slot_mapping, block_tables,
     out, dt, common, ws_ptr, ws_len = _decode_common(
         q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, partition_size, out,
         workspace, kernel)
-    st = _decode_append(_dev(out, "out", ndim=3), _dev(q, "q", ndim=3),
-                        _dev(k_cache, "k_cache", ndim=4), _dev(v_cache, "v_cache", ndim=4),
-                        _dev(k_new, "k_new", ndim=3), _dev(v_new, "v_new", ndim=3),
-                        _dev(slot_mapping, "slot_mapping", torch.int64), *common, float(scale),
-                        int(partition_size), ws_ptr, ws_len, dt, KERNELS[kernel], _stream(stream))
-    _check(st, "decode_append")
+    head = (_dev(out, "out", ndim=3), _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", ndim=4),
+            _dev(v_cache, "v_cache", ndim=4), _dev(k_new, "k_new", ndim=3),
+            _dev(v_new, "v_new", ndim=3), _dev(slot_mapping, "slot_mapping", torch.int64))
+    tail = (float(scale), int(partition_size), ws_ptr, ws_len, dt, KERNELS[kernel],
+            _stream(stream))
+    if order is None:
+        st = _decode_append(*head, *common, *tail)
+        _check(st, "decode_append")
+        return out
+    if order.dim() != 1 or order.shape[0] != B:
+        raise ValueError("order must be [num_seqs]")
+    bt_ptr, maxblk, sl_ptr, mx, *rest = common
+    st = _decode_append_ordered(*head, bt_ptr, maxblk, sl_ptr, mx,
+                                _dev(order, "order", torch.int32), *rest, *tail)
+    _check(st, "decode_append_ordered")
     return out
 
 

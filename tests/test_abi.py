@@ -195,6 +195,19 @@ def test_host_validation_rejects_before_launch(built_lib):
     assert fa(fake, fake, fake, fake, fake, fake, fake, fake, i32(4), fake, i32(16), i32(2),
               i32(8), i32(2), i32(64), i32(16), i32(8), ctypes.c_float(0.1), i32(0), fake,
               ctypes.c_size_t(1 << 26), i32(1), i32(3), none) == INVALID
+    fo = lib.pa_decode_append_ordered
+    fo.restype = ctypes.c_int32
+
+    def fused_ordered(order, slots=fake, B=2, kern=0):
+        return fo(fake, fake, fake, fake, fake, fake, slots, fake, i32(4), fake, i32(16), order,
+                  i32(B), i32(8), i32(2), i32(64), i32(16), i32(8), ctypes.c_float(0.1), i32(0),
+                  fake, ctypes.c_size_t(1 << 20), i32(1), i32(kern), none)
+
+    assert fused_ordered(none) == INVALID                       # no order for 2 sequences
+    assert fused_ordered(fake, slots=none) == INVALID           # no slot mapping
+    assert fused_ordered(vp(4098)) == INVALID                   # order not 4-byte aligned
+    assert fused_ordered(fake, kern=3) == INVALID
+    assert fused_ordered(none, slots=none, B=0) == 0            # empty batch: nothing needed
     cp = lib.pa_copy_blocks
     cp.restype = ctypes.c_int32
     assert cp(fake, fake, fake, i32(-2), i32(8), i32(2), i32(16), i32(64), i32(1), None) == INVALID

@@ -411,6 +411,15 @@ def test_fused_append_decode(pa, kernel, block_size, head_dim):
         torch.cuda.synchronize()
         assert np.array_equal(host(d["k"]), kc) and np.array_equal(host(d["v"]), vc)
         assert_close(as_f64(out), ref, "bf16", f"fused {kernel} b={block_size} d={head_dim} P={partition}")
+        # the ordered call (longest first): same cache, same outputs bit for bit
+        d2 = upload(w)
+        out2 = pa.decode_append(d2["q"], d2["k"], d2["v"], dev(k), dev(v), dev(slots), d2["bt"],
+                                d2["lens"], w.scale, max_seq_len=w.max_seq_len,
+                                partition_size=partition, kernel=kernel,
+                                order=pa.longest_first(d2["lens"]))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(d2["k"]), kc) and np.array_equal(host(d2["v"]), vc)
+        assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
 
 
 def test_fused_append_decode_fp32_tiny(pa):
@@ -429,7 +438,11 @@ def test_fused_append_decode_fp32_tiny(pa):
 
 
 def test_fused_append_decode_full_size(pa):
-    """The benchmark's fused step on the 70B-shaped batch."""
+    """The benchmark's fused step on the 70B-shaped batch, in index order and
+    longest first (pa_decode_append_ordered): the oracle's cache bit for bit,
+    every sequence's output against the oracle, and the outputs of
+    pa_kv_append + pa_decode_ordered bit for bit (the fused launch decodes the
+    appended cache with the same four-wave work-groups)."""
     w = W.llama70b()
     kc, vc = oracle_step(w)
     k, v, slots = W.per_sequence_append(w)
@@ -439,6 +452,18 @@ def test_fused_append_decode_full_size(pa):
     torch.cuda.synchronize()
     assert np.array_equal(host(d["k"]), kc) and np.array_equal(host(d["v"]), vc)
     assert_close(as_f64(out), oracle_decode(w, kc, vc), "bf16", "fused llama70b")
+    order = pa.longest_first(d["lens"])
+    d2 = upload(w)
+    out2 = pa.decode_append(d2["q"], d2["k"], d2["v"], dev(k), dev(v), dev(slots), d2["bt"],
+                            d2["lens"], w.scale, max_seq_len=w.max_seq_len, order=order)
+    d3 = upload(w)
+    pa.kv_append(dev(w.k_new), dev(w.v_new), d3["k"], d3["v"], dev(w.slot_mapping))
+    out3 = pa.decode_ordered(d3["q"], d3["k"], d3["v"], d3["bt"], d3["lens"], order, w.scale,
+                             max_seq_len=w.max_seq_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(d2["k"]), kc) and np.array_equal(host(d2["v"]), vc)
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(out3.view(torch.int16), out.view(torch.int16))
 
 
 @pytest.mark.parametrize("batch", [600, 4500])

@@ -255,3 +255,17 @@ def test_random_fused_append(pa, case):
         assert np.array_equal(raw(host(k)), raw(kc)) and np.array_equal(raw(host(v)), raw(vc)), \
             f"{what} {kernel}: cache"
         assert_close(oracle.to_f64(host(out)), ref, dtype, f"{what} {kernel}")
+        # pa_decode_append_ordered in a random order: the same cache and the
+        # same outputs bit for bit
+        order = torch.from_numpy(rng.permutation(len(pre)).astype(np.int32)).to(DEV)
+        k, v = dev(w.k_cache), dev(w.v_cache)
+        again = pa.decode_append(dev(w.q), k, v, dev(k_new), dev(v_new), dev(slots),
+                                 dev(w.block_tables), dev(lens), w.scale,
+                                 max_seq_len=int(lens.max()), partition_size=part, kernel=kernel,
+                                 order=order)
+        torch.cuda.synchronize()
+        assert np.array_equal(raw(host(k)), raw(kc)) and np.array_equal(raw(host(v)), raw(vc)), \
+            f"{what} {kernel} ordered: cache"
+        assert torch.equal(again.view(torch.int32 if dtype == "f32" else torch.int16),
+                           out.view(torch.int32 if dtype == "f32" else torch.int16)), \
+            f"{what} {kernel}: ordered"

@@ -148,11 +148,9 @@ __device__ inline void load_step(StepRegs<D>& r, const SeqView& c, int base, int
   }
 }
 
-// Scores, online softmax and PV for one loaded step; tokens >= pend masked.
-// kMayBeEmpty: the step can be wholly masked while the wave has seen no token
-// yet (max still -inf); exponents are then taken against 0 so the state stays
-// empty (l = 0, O = 0) instead of turning NaN.
-template <int D, bool kMayBeEmpty = false>
+// Scores, online softmax and PV for one loaded step; tokens >= pend masked
+// (every step holds at least one token below pend: its first).
+template <int D>
 __device__ inline void compute_step(StepRegs<D>& r, Acc<D>& a, const u32x4* qb, int base,
                                     int pend, float scale_log2, int q4) {
   constexpr int kKi = D / 32;
@@ -176,14 +174,13 @@ __device__ inline void compute_step(StepRegs<D>& r, Acc<D>& a, const u32x4* qb, 
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(a.m, mx);
-  const float m_ref = (kMayBeEmpty && m_new == -INFINITY) ? 0.f : m_new;
-  const float keep = __builtin_amdgcn_exp2f(a.m - m_ref);  // 0 on the first step
+  const float keep = __builtin_amdgcn_exp2f(a.m - m_new);  // 0 on the first step
   u32x4 pb;
   float psum = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const uint32_t lo = f32_to_bf16(__builtin_amdgcn_exp2f(t[2 * u] - m_ref));
-    const uint32_t hi = f32_to_bf16(__builtin_amdgcn_exp2f(t[2 * u + 1] - m_ref));
+    const uint32_t lo = f32_to_bf16(__builtin_amdgcn_exp2f(t[2 * u] - m_new));
+    const uint32_t hi = f32_to_bf16(__builtin_amdgcn_exp2f(t[2 * u + 1] - m_new));
     pb[u] = lo | (hi << 16);
     psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
   }

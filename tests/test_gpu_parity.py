@@ -466,6 +466,34 @@ def test_fused_append_decode_full_size(pa):
     assert torch.equal(out3.view(torch.int16), out.view(torch.int16))
 
 
+def test_fused_append_ordered_entry_outside_the_batch(pa):
+    """pa_decode_append_ordered: an order entry outside the batch leaves its
+    work-group idle, so the sequence it replaced gets neither its output row
+    nor its append; every other sequence's append and output are right."""
+    w = _fused_case(16, 128, skip=())
+    kc, vc = oracle_step(w)
+    k, v, slots = W.per_sequence_append(w)
+    d = upload(w)
+    order = pa.longest_first(d["lens"]).clone()
+    missing = int(order[3])
+    order[3] = w.num_seqs + 7                          # outside the batch: slot 3 idles
+    out = torch.full_like(d["q"], 7.0)
+    pa.decode_append(d["q"], d["k"], d["v"], dev(k), dev(v), dev(slots), d["bt"], d["lens"],
+                     w.scale, max_seq_len=w.max_seq_len, out=out, order=order)
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    assert np.all(got[missing] == 7.0)                 # its row was never written
+    kh, vh = host(d["k"]), host(d["v"])
+    slot = int(slots[missing])
+    blk, off = slot // w.block_size, slot % w.block_size
+    assert np.array_equal(kh[blk, :, off], w.k_cache[blk, :, off])   # its append did not happen
+    rest = [s for s in range(w.num_seqs) if s != missing]
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[blk, :, off], vc2[blk, :, off] = w.k_cache[blk, :, off], w.v_cache[blk, :, off]
+    assert np.array_equal(kh, kc2) and np.array_equal(vh, vc2)
+    assert_close(got[rest], oracle_decode(w, kc, vc, seqs=rest), "bf16", "fused ordered, idle slot")
+
+
 @pytest.mark.parametrize("batch", [600, 4500])
 def test_longest_first_ranking_large_batches(pa, batch):
     """Batches past the ranking's in-register lengths (> 512 sequences: lengths

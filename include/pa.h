@@ -492,7 +492,8 @@ pa_status pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_num_blocks, const
  * [kv_heads][block_size][head_dim] -- a block holds the K (index 0) and V
  * (index 1) of all layers for its block_size tokens (zenaique.com code box
  * "Conceptual: PagedAttention block lookup"; "How PagedAttention works",
- * section "A strong answer": one pool per layer or a layered layout).  One
+ * section "A strong answer": a pool for each layer, or one pool holding all
+ * layers).  One
  * block table per sequence serves every layer; slots and block ids mean the
  * same as for per-layer pools.  Same element types, shapes, errors and
  * device-content behaviour as the per-layer calls, plus: layer indices out

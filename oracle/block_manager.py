@@ -5,12 +5,12 @@ one behind include/pa.h (pa_bm_*), which shares no code with it.
 
 What the pages fix:
 
-* "How PagedAttention works", section "A strong answer": the pool is carved
-  into equal blocks, each sequence owns a block table, only the last block of
-  a sequence is partly filled; the feature table: a shared prefix is one set of
-  blocks with a reference count per block, a fork shares blocks and copies
-  only the block that diverges (copy on write), preemption swaps blocks to
-  host memory at block granularity;
+* "How PagedAttention works", section "A strong answer": the pool is split
+  into blocks of one size, every sequence has its own table of block ids, at
+  most a sequence's final block has unused slots; the feature table: a shared
+  prefix is a single set of blocks counted by reference, a fork shares its
+  parent's blocks and copies a block only when a branch writes to it (copy on
+  write), preemption moves whole blocks out to host memory;
 * same page, section "What interviewers probe next": admitting a request needs
   ceil(prompt tokens / block size) free blocks plus at least one to grow into,
   and a small watermark reserve is kept so decode steps do not starve;

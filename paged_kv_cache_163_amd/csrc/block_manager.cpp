@@ -1,14 +1,15 @@
 // Host-side block bookkeeping of the paged KV cache (include/pa.h, pa_bm_*):
 // the steps either side of pa_kv_append / pa_copy_blocks / pa_swap_blocks.
 //
-// "How PagedAttention works", section "A strong answer": the pool is carved
-// into equal blocks, each sequence owns a block table and only its last block
-// is partly filled; the feature table: a shared prefix is one set of blocks
-// with a reference count per block, a fork shares blocks and copies only the
-// block that diverges, preemption swaps blocks to host memory at block
-// granularity.  Section "What interviewers probe next": admission needs
-// ceil(prompt / block size) free blocks plus one to grow into, above a small
-// watermark reserve.
+// "How PagedAttention works", section "A strong answer": the pool is split
+// into blocks of one size, every sequence has its own table of block ids and
+// at most its final block has unused slots; the feature table: a shared
+// prefix is a single set of blocks counted by reference, a fork shares its
+// parent's blocks and copies a block only when one branch writes to it,
+// preemption moves whole blocks out to host memory.  Section "What
+// interviewers probe next": a request is admitted when the pool has
+// ceil(prompt / block size) blocks for it plus one to grow into, above a
+// small watermark reserve.
 //
 // Policies the pages leave open: the lowest-numbered free block is taken
 // first (so placements are reproducible); the watermark gates admission only;

@@ -13,8 +13,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-// Append ("How PagedAttention works", section "A strong answer": the cache
-// grows by one token per decode step).  Token i's row for KV head h goes to
+// Append ("How PagedAttention works", section "A strong answer": each decode
+// step adds one token's K and V to its sequence's cache).  Token i's row for KV head h goes to
 // physical block slot/block_size, slot slot%block_size; blocks lie
 // block_vecs 16-byte vectors apart (kv_heads * block_size * row_vecs for a
 // per-layer pool, more in a layered pool where k_cache / v_cache point at

@@ -121,7 +121,7 @@ def test_engine_steps_through_the_native_block_manager(pa):
     assert len(cow) == 1
     e.check_pools()
 
-    # preempt sequence 2: swap its blocks to pinned host memory, run without it
+    # preempt sequence 2: move its blocks out to pinned host buffers, run without it
     pairs = np.array(e.bm.swap_out(2), dtype=np.int64)
     pa.swap_blocks(e.ghk, e.ghv, e.gk, e.gv, dev(pairs))
     oracle.swap_blocks(e.hk, e.hv, e.k, e.v, pairs)

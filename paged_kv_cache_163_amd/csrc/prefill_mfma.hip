@@ -104,6 +104,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     a[nr].l = f32x4{0.f, 0.f, 0.f, 0.f};
     a[nr].m = -INFINITY;
+    a[nr].thr = -INFINITY;
   }
   bool bad = false;
   // Q^T operands of the lane's row in each tile (zero past the chunk) and the
@@ -126,7 +127,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     }
   };
   __shared__ __attribute__((aligned(1024))) unsigned char sm_b[kLdsBufs][kStepBytes<D>];
-  attend_keys<D>(a, c, qb, lim, 0, kend_wg, kend, kfull, wave_rows, p.scale_log2, bad, sm_b, wave,
+  attend_keys<D>(a, c, qb, lim, 0, kend_wg, kend, len, kfull, wave_rows, p.scale_log2, bad, sm_b, wave,
                  lane, load_q);
   __syncthreads();   // every wave is done reading the buffers the output staging reuses
   if (!wave_rows) return;

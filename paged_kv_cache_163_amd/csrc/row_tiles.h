@@ -36,6 +36,7 @@ struct PfAcc {
   f32x4 o[D / 16];
   f32x4 l;
   float m;
+  float thr;  // m + kSlack: a step max above it rescales
 };
 
 // How far (base-2 units) a row's step max may rise above its reference max
@@ -50,22 +51,16 @@ struct MaskTag {
 };
 
 // Max over the four lanes that share r16 (one per 16-lane row of the wave).
-// The maxes are plain v_max_f32, written as assembly: fmaxf on values that
-// come from a lane swap adds two signaling-NaN quieting maxes per call, which
-// these operands (scores, or -inf) never need.
-__device__ inline float fmax_nonan(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
+// The maxes here and in the step are the NaN-propagating maximum
+// (v_maximum3_f32): unlike fmaxf's maxnum it needs no quieting of its
+// operands, and on the scores (never NaN) the two agree.
 __device__ inline float row_max4(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = fmax_nonan(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t w = __float_as_uint(x);
   const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmax_nonan(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -81,18 +76,25 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // Softmax and PV of one 32-key step for all row tiles of a wave, from its
 // raw scores s.  kMask (a step that some row of the wave does not see whole:
 // it reaches past kfull, the wave's first row position) masks keys > lim[nr]
-// (the lane's row position) and zeroes the V values of keys at or past kend,
-// the wave's last key + 1; other steps need neither.  The row tiles go
-// through the step together with one wave-uniform rescale branch, so their
-// dependent max and exp chains interleave.
-// c = scale * log2(e) > 0 (the host rejects other scales), so the row max of
-// c*s is c times the max of s.  A row tile whose keys are all masked in a
-// step has mx = -inf: its reference max stays and its probabilities are 0
-// (every tile sees a finite key in its first step).
+// (the lane's row position); if the step also reaches kvalid, the first key
+// that may hold anything but finite data (tail slots past the sequence), it
+// zeroes the V values of keys from there on, since a zero probability times
+// a NaN would still reach the sum.  Unmasked steps need neither.  The row
+// tiles go through the step together with one wave-uniform rescale branch,
+// so their dependent max and exp chains interleave.
+// c = scale * log2(e) > 0 (the host rejects other scales), so c times a max
+// of s is the max of c*s, rounding included (rounding is monotonic).  The
+// rescale test therefore needs only each lane's own max: a row's max over
+// its four lanes exceeds the threshold exactly when one lane's does, and the
+// lane exchange runs only inside the (rare) rescale branch.  A row tile
+// whose keys are all masked in a step has a max of -inf: its reference max
+// stays and its probabilities are 0 (every tile sees a finite key in its
+// first step).
 template <int D, bool kMask>
 __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&av)[D / 16],
-                                       PfAcc<D> (&a)[kRowTiles], int base, int kend,
-                                       const int (&lim)[kRowTiles], float c, int q4) {
+                                       PfAcc<D> (&a)[kRowTiles], int base, int kvalid,
+                                       const int (&lim)[kRowTiles], float c, int q4,
+                                       const u32x4& ones) {
   constexpr int kVd = D / 16;
   float sv[kRowTiles][8];
 #pragma unroll
@@ -100,16 +102,18 @@ __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&a
 #pragma unroll
     for (int e = 0; e < 8; ++e) sv[nr][e] = s[nr][e >> 2][e & 3];
   if constexpr (kMask) {
-    uint32_t keep[4];
+    if (base + 32 > kvalid) {  // wave-uniform: the step reaches past the live keys
+      uint32_t keep[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int tok = base + 16 * (u >> 1) + 4 * q4 + 2 * (u & 1);
-      keep[u] = (tok < kend ? 0x0000FFFFu : 0u) | (tok + 1 < kend ? 0xFFFF0000u : 0u);
+      for (int u = 0; u < 4; ++u) {
+        const int tok = base + 16 * (u >> 1) + 4 * q4 + 2 * (u & 1);
+        keep[u] = (tok < kvalid ? 0x0000FFFFu : 0u) | (tok + 1 < kvalid ? 0xFFFF0000u : 0u);
+      }
+#pragma unroll
+      for (int jt = 0; jt < kVd; ++jt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) av[jt][u] &= keep[u];
     }
-#pragma unroll
-    for (int jt = 0; jt < kVd; ++jt)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) av[jt][u] &= keep[u];
 #pragma unroll
     for (int nr = 0; nr < kRowTiles; ++nr)
 #pragma unroll
@@ -118,26 +122,25 @@ __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&a
         sv[nr][e] = tok <= lim[nr] ? sv[nr][e] : -INFINITY;
       }
   }
-  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  float mx[kRowTiles];
+  float mr[kRowTiles];
   bool grow = false;
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr) {
-    float mr = sv[nr][0];
+    mr[nr] = sv[nr][0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mr = fmaxf(mr, sv[nr][e]);
-    mx[nr] = row_max4(mr) * c;
-    grow |= mx[nr] > a[nr].m + kSlack;
+    for (int e = 1; e < 8; ++e) mr[nr] = __builtin_elementwise_maximum(mr[nr], sv[nr][e]);
+    grow |= mr[nr] * c > a[nr].thr;
   }
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
 #pragma unroll
     for (int nr = 0; nr < kRowTiles; ++nr) {
-      const float m_new = fmaxf(a[nr].m, mx[nr]);
+      const float m_new = fmaxf(a[nr].m, row_max4(mr[nr]) * c);
       const float keep = __builtin_amdgcn_exp2f(a[nr].m - m_new);  // 0 on the first step
 #pragma unroll
       for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] *= keep;
       a[nr].l *= keep;
       a[nr].m = m_new;
+      a[nr].thr = m_new + kSlack;
     }
   }
   // Tile 0's probabilities first.  Its products then go to the matrix cores a
@@ -171,16 +174,20 @@ __device__ inline void step_softmax_pv(const f32x4 (&s)[kRowTiles][2], u32x4 (&a
 // Direct global-to-LDS staging (global_load_lds_dwordx4).  One instruction
 // moves 16 bytes per lane straight into LDS: lane l's bytes land at the
 // wave-uniform LDS address + 16 l, so each instruction fills one contiguous
-// 1 KiB block.  A step's K and V tiles are D/16 such blocks each (K first);
-// block j of a tile holds the 16-byte chunks 2j and 2j + 1 of all 32 rows,
-// chunk c of row r at lane
-//   16 (2 (r / 16) + (c & 1)) + (r % 16)               in a K block,
-//   16 (2 (r / 16) + (c & 1)) + ((r % 16) ^ 8 (c & 1)) in a V block.
+// 1 KiB block.  A step's K and V tiles are D/16 such blocks each (K first).
+// Every block comes from one 16-token tile of the cache (rows 16 h .. 16 h +
+// 15 of the step), so an instruction reads from one wave-uniform base
+// address in scalar registers plus a fixed 32-bit offset per lane, and the
+// step's address arithmetic stays on the scalar unit.  Block h * D/32 + j of
+// a tile holds the 16-byte chunks 4j .. 4j + 3 of those 16 rows, chunk
+// 4j + cc of row r at lane
+//   16 cc + r                   in a K block,
+//   16 cc + (r ^ 8 (cc & 1))    in a V block.
 // Measured with a bank-conflict probe on gfx950: the K operand reads
-// (ds_read_b128, 16 rows of one chunk) are conflict-free on the plain layout
-// and 2-way on the XOR one, the V transpose reads (ds_read_b64_tr_b16, rows
-// 0..7 of chunks 2j and 2j + 1 per half-wave) the other way round.  Wave w
-// issues blocks w, w + kPfWaves, ... of a step.
+// (ds_read_b128, 16 rows of one chunk) are then one contiguous 1 KiB and
+// conflict-free; the V transpose reads (ds_read_b64_tr_b16, rows 0..7 of two
+// adjacent chunks per half-wave) are conflict-free with the XOR and 2-way
+// without it.  Wave w issues blocks w, w + kPfWaves, ... of a step.
 constexpr int kLdsBufs = 4;                        // LDS buffers; steps staged ahead: 3
 template <int D>
 constexpr int kTileBytes = 32 * D * 2;             // one K or V tile of a step
@@ -196,23 +203,25 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int D>
 struct DmaLane {
   uint32_t off[kDmaPerWave<D>];  // byte offset inside the 16-token block tile
-  bool hi;                       // the lane's row is in the step's second 16-token tile
   bool v[kDmaPerWave<D>];        // wave-uniform: the instruction stages V
+  bool hi[kDmaPerWave<D>];       // wave-uniform: it stages the step's second 16-token tile
 };
 
 template <int D>
 __device__ inline DmaLane<D> dma_lane(int wave, int lane) {
+  constexpr int kPer = D / 32;  // 1 KiB blocks per 16-token tile of K or V
   DmaLane<D> dl;
-  const int g = lane >> 4;
-  const int b = g & 1;
-  dl.hi = g >= 2;
+  const int cc = lane >> 4;
+  const int s16 = lane & 15;
 #pragma unroll
   for (int u = 0; u < kDmaPerWave<D>; ++u) {
     const int bi = u * kPfWaves + wave;
-    const int j = bi % (D / 16);
-    dl.v[u] = bi >= D / 16;
-    const int rr = dl.v[u] ? (lane & 15) ^ (8 * b) : lane & 15;  // row in the 16-token tile
-    dl.off[u] = (uint32_t)(rr * (D * 2) + 16 * (2 * j + b));
+    dl.v[u] = bi >= 2 * kPer;
+    const int kb = dl.v[u] ? bi - 2 * kPer : bi;
+    dl.hi[u] = kb >= kPer;
+    const int j = kb % kPer;
+    const int rr = dl.v[u] ? s16 ^ (8 * (cc & 1)) : s16;  // row in the 16-token tile
+    dl.off[u] = (uint32_t)(rr * (D * 2) + 16 * (4 * j + cc));
   }
   return dl;
 }
@@ -239,22 +248,23 @@ __device__ inline void lds_barrier() {
 }
 
 // One 16-byte-per-lane direct load into LDS (lane l's bytes at lds + 16 l;
-// M0 holds the wave-uniform LDS address and is restored afterwards).
+// M0 holds the wave-uniform LDS address and is restored afterwards) from the
+// wave-uniform address `base` plus the lane's 32-bit offset.
 // Written as inline assembly so that the compiler does not track it: its own
 // tracking waits for every staging load in flight before the LDS transpose
 // reads of any buffer.  Completion is awaited explicitly (dma_wait) before a
 // buffer is read.
-__device__ inline void dma16(const char* src, unsigned char* lds) {
+__device__ inline void dma16(const char* base, uint32_t off, unsigned char* lds) {
   const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)lds;
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(m)
+      : "v"(off), "s"(base), "s"(m)
       : "memory");
 }
 
@@ -278,22 +288,21 @@ __device__ inline void dma_issue(const DmaLane<D>& dl, const SeqView& c, int wav
     }
     tile[kt] = (int64_t)phys[kt] * c.block_stride + (int64_t)(tok0 & c.bmask) * (D * 2);
   }
-  const int64_t t = dl.hi ? tile[1] : tile[0];
-  const char* kp = c.kbase + t;
-  const char* vp = c.vbase + t;
 #pragma unroll
   for (int u = 0; u < kDmaPerWave<D>; ++u) {
     const int bi = u * kPfWaves + wave;
-    dma16((dl.v[u] ? vp : kp) + dl.off[u], buf + 1024 * bi);
+    dma16((dl.v[u] ? c.vbase : c.kbase) + (dl.hi[u] ? tile[1] : tile[0]), dl.off[u],
+          buf + 1024 * bi);
   }
 }
 
 // Byte offsets of lane (r16, q4)'s K operand reads (row 16 kt + r16, chunk
-// 4 i + q4, at + 2048 i + 512 kt) and V transpose reads (key 4 q4 + r16 / 4
-// (+ 16), head dims 16 jt + 4 (r16 % 4) .. + 3, at + 1024 jt (+ 512)) in a
-// staged step; the V offset is relative to the V tile.
+// 4 i + q4, at + 1024 (kt D/32 + i)) and V transpose reads (key 4 q4 + r16 / 4
+// (+ 16), head dims 16 jt + 4 (r16 % 4) .. + 3, at + 1024 (jt / 2) + 512 (jt
+// % 2) (+ 1024 D/32)) in a staged step; the V offset is relative to the V
+// tile.
 __device__ inline uint32_t dma_k_lane(int r16, int q4) {
-  return 1024 * (q4 >> 1) + 256 * (q4 & 1) + 16 * r16;
+  return 16 * (16 * q4 + r16);
 }
 __device__ inline uint32_t dma_v_lane(int r16, int q4) {
   const int b = (r16 >> 1) & 1;
@@ -317,7 +326,7 @@ __device__ inline void step_scores(f32x4 (&s)[kRowTiles][2], const unsigned char
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) k[i][kt] = *(const u32x4*)(ks + 2048 * i + 512 * kt);
+    for (int kt = 0; kt < 2; ++kt) k[i][kt] = *(const u32x4*)(ks + 1024 * (kt * (D / 32) + i));
   // Tile 0 first: its running max can then be taken while tile 1's products run.
 #pragma unroll
   for (int nr = 0; nr < kRowTiles; ++nr)
@@ -339,8 +348,9 @@ template <int D>
 __device__ inline void read_v(u32x4 (&av)[D / 16], const unsigned char* v0) {
 #pragma unroll
   for (int jt = 0; jt < D / 16; ++jt) {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 1024 * jt));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 1024 * jt + 512));
+    const unsigned char* p = v0 + 1024 * (jt >> 1) + 512 * (jt & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 1024 * (D / 32)));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
     const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
     av[jt] = u32x4{l2[0], l2[1], h2[0], h2[1]};
@@ -377,7 +387,8 @@ template <int D, class LoadQ>
 __device__ inline void attend_keys(PfAcc<D> (&a)[kRowTiles], const SeqView& c,
                                    const u32x4 (&qb)[kRowTiles][D / 32],
                                    const int (&lim)[kRowTiles], int kstart, int kend_wg,
-                                   int kend, int kfull, bool wave_rows, float scale_log2,
+                                   int kend, int kvalid, int kfull, bool wave_rows,
+                                   float scale_log2,
                                    bool& bad, unsigned char (*buf)[kStepBytes<D>], int wave,
                                    int lane, LoadQ&& load_q) {
   const int r16 = lane & 15;
@@ -385,6 +396,9 @@ __device__ inline void attend_keys(PfAcc<D> (&a)[kRowTiles], const SeqView& c,
   const DmaLane<D> dl = dma_lane<D>(wave, lane);
   const uint32_t kl = dma_k_lane(r16, q4);
   const uint32_t vl = kTileBytes<D> + dma_v_lane(r16, q4);
+  // The row sums' ones operand, held in registers for the whole walk.
+  u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  asm volatile("" : "+v"(ones));
   const int nsteps = (kend_wg - kstart + 31) >> 5;
   if (nsteps <= 0) {  // no keys: nothing staged, so nothing in flight at exit
     load_q();
@@ -408,7 +422,7 @@ __device__ inline void attend_keys(PfAcc<D> (&a)[kRowTiles], const SeqView& c,
       step_scores<D>(s, cur + kl, qb);
       u32x4 av[D / 16];
       read_v<D>(av, cur + vl);
-      step_softmax_pv<D, kMask>(s, av, a, base, kend, lim, scale_log2, q4);
+      step_softmax_pv<D, kMask>(s, av, a, base, kvalid, lim, scale_log2, q4, ones);
     }
   };
   // Unmasked steps: base + 31 <= kfull (then also base < kend).  They come in

@@ -90,6 +90,7 @@ __device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x,
     for (int jt = 0; jt < kVd; ++jt) a[nr].o[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
     a[nr].l = f32x4{0.f, 0.f, 0.f, 0.f};
     a[nr].m = -INFINITY;
+    a[nr].thr = -INFINITY;
   }
   bool bad = false;
   // Q^T operands of the lane's row (a member's query head; zero past the
@@ -112,7 +113,7 @@ __device__ __forceinline__ void prefix_wg(const DecodeParams& p, int x,
         qb[nr][i] = valid ? *(const u32x4*)(qrow + 64 * i) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  attend_keys<D>(a, c, qb, lim, kstart, kend_wg, kend, kfull, wave_rows, p.scale_log2, bad, buf,
+  attend_keys<D>(a, c, qb, lim, kstart, kend_wg, kend, kend, kfull, wave_rows, p.scale_log2, bad, buf,
                  wave, lane, load_q);
   if (!wave_rows) return;
 

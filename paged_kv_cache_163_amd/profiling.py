@@ -38,15 +38,38 @@ def _csv(directory: str, suffix: str) -> list[dict]:
         return list(csv.DictReader(f))
 
 
+TAIL_CALLS = 100   # the benchmark's timed launches come last in its run
+
+
+def _tail_avg_us(trace_dir: str) -> dict:
+    """Average duration (us) of each kernel's last TAIL_CALLS dispatches in
+    the kernel trace: the steady state after the run's warm-up launches."""
+    try:
+        rows = _csv(trace_dir, "kernel_trace.csv")
+    except FileNotFoundError:
+        return {}
+    per = {}
+    for r in rows:
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, d in per.items():
+        tail = [ns for _, ns in sorted(d)[-TAIL_CALLS:]]
+        out[name] = sum(tail) / len(tail) / 1e3
+    return out
+
+
 def kernel_stats_md(trace_dir: str, command: str) -> str:
     rows = _csv(trace_dir, "kernel_stats.csv")
+    tail = _tail_avg_us(trace_dir)
     lines = [f"Command: `{command}`", "",
-             "| kernel | calls | avg us | min us | max us | share % |",
-             "|---|---|---|---|---|---|"]
+             f"| kernel | calls | avg us | min us | max us | share % | avg us, last {TAIL_CALLS} calls |",
+             "|---|---|---|---|---|---|---|"]
     for r in rows:
+        t = tail.get(r["Name"])
         lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{float(r['Percentage']):.2f} |")
+                     f"{float(r['Percentage']):.2f} | {'' if t is None else f'{t:.2f}'} |")
     return "\n".join(lines) + "\n"
 
 

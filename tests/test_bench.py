@@ -73,6 +73,23 @@ def test_traffic_scales_counters_by_the_copy_calibration(tmp_path):
     assert rec["dispatches"] == 3
 
 
+def test_kernel_stats_add_the_steady_state_of_the_last_calls(tmp_path):
+    from paged_kv_cache_163_amd import profiling as P
+    with open(tmp_path / "x_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"])
+        w.writerow(["k", 150, 0, 5000.0, 100.0, 1000.0, 9000.0])
+    # 50 slow warm-up calls of 9 us, then 100 of 1 us, written out of order
+    calls = [(1000 * i, 9000) for i in range(50)] + [(1000 * i, 1000) for i in range(50, 150)]
+    with open(tmp_path / "x_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for start, dur in reversed(calls):
+            w.writerow(["k", start, start + dur])
+    md = P.kernel_stats_md(str(tmp_path), "cmd")
+    assert "| k | 150 | 5.00 | 1.00 | 9.00 | 100.00 | 1.00 |" in md
+
+
 def test_counter_summary_sums_per_dispatch_and_takes_the_median(tmp_path):
     from paged_kv_cache_163_amd import profiling as P
     rows = []

@@ -291,8 +291,15 @@ __device__ inline void dma_issue(const DmaLane<D>& dl, const SeqView& c, int wav
 #pragma unroll
   for (int u = 0; u < kDmaPerWave<D>; ++u) {
     const int bi = u * kPfWaves + wave;
-    dma16((dl.v[u] ? c.vbase : c.kbase) + (dl.hi[u] ? tile[1] : tile[0]), dl.off[u],
-          buf + 1024 * bi);
+    // When each 16-token tile of K or V is kPfWaves blocks (head_dim 128),
+    // instruction u of every wave stages the same kind of block: K for the
+    // first half of the instructions, V for the second, the step's second
+    // tile for odd u.  The choice is then a compile-time one, with no scalar
+    // selects per instruction.
+    constexpr bool kFixed = D / 32 == kPfWaves;
+    const bool v = kFixed ? u >= kDmaPerWave<D> / 2 : dl.v[u];
+    const bool hi = kFixed ? (u & 1) != 0 : dl.hi[u];
+    dma16((v ? c.vbase : c.kbase) + (hi ? tile[1] : tile[0]), dl.off[u], buf + 1024 * bi);
   }
 }
 
